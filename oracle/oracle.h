@@ -1,0 +1,89 @@
+/*
+ * oracle.h - CPU reference ("oracle") of the DeepSeek-style MoE layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Plain, slow, obviously correct C.  Only the tests,
+ * the package's smoke check and the benchmark's CPU-baseline leg may load it; the
+ * GPU library never links or calls it, and the two share no code.  Inputs come
+ * from the separate `synth` generator.
+ *
+ * Sources (pages given by title):
+ *   [PR123]  "feat(engine): E1 DeepSeek-style MoE gate (sigmoid, group top-k, bias) (#108)"
+ *            - sections "API", "Algorithm (mlx-lm group_expert_select)", "Scope decisions",
+ *              and the two code reviews (validation matrix, S1/S2/S5, D7, zero-sum note,
+ *              masked-to-zero non-issue).
+ *   [Epic56] "Epic: Engine Inference Core Stage E - MoE + hybrid families"
+ *            - opening paragraph (expert dispatch via gather_qmm / gather_mm) and
+ *              "Decision 5 superseded" item 2 (sigmoid gating, group selection, shared
+ *              experts always active).
+ *
+ * Precision: the gate is fp32 because [PR123] "Algorithm" casts the gate logits to f32
+ * before the sigmoid.  The router dot product is fp32 with a fixed order (see
+ * oracle_router).  The expert SwiGLU, shared expert and combine are computed in fp64
+ * (at least the fp32 accumulation the layer requires).
+ *
+ * Dtype codes: 0 = fp32, 1 = bf16 (uint16 bit patterns), 2 = 4-bit affine, group 64.
+ */
+#ifndef DSMOE_ORACLE_H
+#define DSMOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct oracle_route_params {
+    int32_t top_k;
+    int32_t n_group;
+    int32_t topk_group;
+    int32_t norm_topk_prob;
+    float routed_scaling_factor;
+} oracle_route_params;
+
+typedef struct oracle_layer {
+    int64_t T;
+    int32_t H, E, I, Is; /* Is == 0: no shared expert */
+    int32_t act;         /* 0 fp32, 1 bf16: x, router, shared weights */
+    int32_t expert;      /* 0 fp32, 1 bf16, 2 q4g64: routed expert weights */
+    oracle_route_params route;
+    const void* x;        /* [T,H] act */
+    const void* router;   /* [E,H] act */
+    const float* bias;    /* [E] e_score_correction_bias */
+    const float* offset;  /* NULL or [E]: added to the router logits */
+    const void* wg;       /* [E,I,H] (q4: uint32 [E,I,H/8]) */
+    const void* wu;       /* [E,I,H] */
+    const void* wd;       /* [E,H,I] (q4: uint32 [E,H,I/8]) */
+    const uint16_t *sg, *bg, *su, *bu, *sd, *bd; /* q4 only: bf16 scale / offset [E,out,in/64] */
+    const void* swg;      /* [Is,H] act */
+    const void* swu;      /* [Is,H] act */
+    const void* swd;      /* [H,Is] act */
+} oracle_layer;
+
+/* exp by Cody-Waite range reduction + degree-7 Taylor polynomial, fp32 (see oracle.c) */
+float oracle_exp(float x);
+/* 1 / (1 + oracle_exp(-x)), IEEE fp32 division */
+float oracle_sigmoid(float x);
+
+/* Router: logits[t,e] = sum_k x[t,k]*W[e,k] (fp32 fma, k ascending from 0) [+ offset[e]]. */
+void oracle_router(const void* x, const void* w, int32_t dtype, int64_t T, int32_t H, int32_t E,
+                   const float* offset, float* logits);
+
+/* DeepSeek gate over T rows.  Returns 0, or -1 on invalid arguments (outputs untouched). */
+int oracle_route(const float* logits, int64_t T, int32_t E, const float* bias, const oracle_route_params* p,
+                 int32_t* inds, float* scores);
+
+/* SwiGLU expert on one fp64 input row: out[H] = W_down (silu(W_gate x) * (W_up x)).
+ * w* point at ONE expert's matrices in `dtype`; s*, b* are its q4 scale/offset (or NULL). */
+void oracle_swiglu(const double* x, int32_t H, int32_t I, int32_t dtype, const void* wg, const void* wu,
+                   const void* wd, const uint16_t* sg, const uint16_t* bg, const uint16_t* su,
+                   const uint16_t* bu, const uint16_t* sd, const uint16_t* bd, double* out);
+
+/* Whole layer for the tokens rows[0..n_rows) (rows == NULL: all T tokens in order).
+ * y: fp64 [n_rows,H]; inds/scores: [n_rows,K] (may be NULL); logits: [n_rows,E] (may be NULL).
+ * Returns 0, or -1 on invalid arguments. */
+int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, double* y, int32_t* inds,
+                   float* scores, float* logits);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

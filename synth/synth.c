@@ -1,0 +1,135 @@
+/*
+ * synth.c - seeded, counter-based synthetic inputs for the MoE layer.
+ *
+ * This module only MAKES inputs (activations, weights, biases, 4-bit packed
+ * weights).  It holds none of the layer's arithmetic: no sigmoid, no routing,
+ * no matmul.  Both the CPU oracle and the GPU path read what it writes.
+ *
+ * Generator: every element i of tensor `tid` under seed `seed` is a pure
+ * function of (seed, tid, i), so any element can be regenerated on its own and
+ * the result does not depend on thread count or chunking.
+ *   - uniform bits: the SplitMix64 output function (Steele, Lea, Flood,
+ *     "Fast splittable pseudorandom number generators", OOPSLA 2014) applied
+ *     to a Weyl sequence key + (counter+1) * golden-gamma;
+ *   - normals: the Box-Muller transform in double precision, one pair of
+ *     uniforms per pair of elements (even element -> cosine branch, odd ->
+ *     sine branch);
+ *   - bf16: the double is rounded to fp32, then fp32 -> bf16 with
+ *     round-to-nearest-even.
+ * 4-bit affine group quantisation (groups of 64 along the input axis):
+ *   s = bf16((max-min)/15), b = bf16(min), q = clamp(rint((w-b)/s), 0, 15),
+ *   q = 0 when s == 0; eight 4-bit codes per uint32, element i at bits 4*(i%8).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define GAMMA 0x9E3779B97F4A7C15ULL
+
+static inline uint64_t sm_mix(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+static inline uint64_t key_of(uint64_t seed, uint64_t tid) {
+    return sm_mix(sm_mix(seed * GAMMA + 0x243F6A8885A308D3ULL) + tid * GAMMA);
+}
+
+/* 64 random bits for counter c of stream `key` */
+static inline uint64_t bits_at(uint64_t key, uint64_t c) { return sm_mix(key + (c + 1) * GAMMA); }
+
+uint64_t synth_bits(uint64_t seed, uint64_t tid, uint64_t c) { return bits_at(key_of(seed, tid), c); }
+
+/* standard normal for element i (Box-Muller on the pair i/2) */
+static inline double normal_at(uint64_t key, uint64_t i) {
+    uint64_t p = i >> 1;
+    uint64_t a = bits_at(key, 2 * p), b = bits_at(key, 2 * p + 1);
+    double u1 = ((double)(a >> 11) + 0.5) * 0x1.0p-53; /* (0,1) */
+    double u2 = (double)(b >> 11) * 0x1.0p-53;         /* [0,1) */
+    double r = sqrt(-2.0 * log(u1));
+    double t = 6.283185307179586476925286766559 * u2;
+    return (i & 1) ? r * sin(t) : r * cos(t);
+}
+
+static inline uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40); /* quiet NaN */
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+static inline float bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* out[j] = float(std * N(0,1) element (start+j)) + mean */
+void synth_normal_f32(uint64_t seed, uint64_t tid, uint64_t start, int64_t n, double mean, double std,
+                      float* out) {
+    uint64_t key = key_of(seed, tid);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) out[j] = (float)(mean + std * normal_at(key, start + (uint64_t)j));
+}
+
+void synth_normal_bf16(uint64_t seed, uint64_t tid, uint64_t start, int64_t n, double mean, double std,
+                       uint16_t* out) {
+    uint64_t key = key_of(seed, tid);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j)
+        out[j] = f32_to_bf16_rne((float)(mean + std * normal_at(key, start + (uint64_t)j)));
+}
+
+/* fp32 -> bf16 (RNE) conversion of an existing buffer */
+void synth_f32_to_bf16(const float* in, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) out[j] = f32_to_bf16_rne(in[j]);
+}
+
+/*
+ * 4-bit affine quantisation of `rows` rows of length `cols` (cols % 64 == 0) whose fp32
+ * values are the normals of tensor (seed, tid) starting at element `start`, scaled by std.
+ * q:  uint32 [rows, cols/8]; s, b: bf16 [rows, cols/64].
+ */
+void synth_q4_normal(uint64_t seed, uint64_t tid, uint64_t start, int64_t rows, int64_t cols, double std,
+                     uint32_t* q, uint16_t* s, uint16_t* b) {
+    uint64_t key = key_of(seed, tid);
+    int64_t ng = cols / 64;
+#pragma omp parallel for schedule(static)
+    for (int64_t rg = 0; rg < rows * ng; ++rg) {
+        int64_t r = rg / ng, g = rg % ng;
+        float w[64];
+        uint64_t base = start + (uint64_t)(r * cols + g * 64);
+        float mn = INFINITY, mx = -INFINITY;
+        for (int i = 0; i < 64; ++i) {
+            w[i] = (float)(std * normal_at(key, base + (uint64_t)i));
+            if (w[i] < mn) mn = w[i];
+            if (w[i] > mx) mx = w[i];
+        }
+        uint16_t sb = f32_to_bf16_rne((mx - mn) / 15.0f);
+        uint16_t bb = f32_to_bf16_rne(mn);
+        float sf = bf16_to_f32(sb), bf = bf16_to_f32(bb);
+        uint32_t* qw = q + r * (cols / 8) + g * 8;
+        for (int k = 0; k < 8; ++k) qw[k] = 0;
+        for (int i = 0; i < 64; ++i) {
+            int code = 0;
+            if (sf != 0.0f) {
+                float v = rintf((w[i] - bf) / sf);
+                code = v < 0.0f ? 0 : (v > 15.0f ? 15 : (int)v);
+            }
+            qw[i / 8] |= (uint32_t)code << (4 * (i % 8));
+        }
+        s[r * ng + g] = sb;
+        b[r * ng + g] = bb;
+    }
+}
+
+/* out[j] = uniform [0,1) double from the 53 high bits of counter start+j */
+void synth_uniform_f64(uint64_t seed, uint64_t tid, uint64_t start, int64_t n, double* out) {
+    uint64_t key = key_of(seed, tid);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j) out[j] = (double)(bits_at(key, start + (uint64_t)j) >> 11) * 0x1.0p-53;
+}
