@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeepSeek-V3-shaped MoE layer forward on one MI355X.
+
+One "step" is one moe_forward call: router -> gate -> dispatch -> grouped gate/up GEMM with
+SwiGLU -> grouped down GEMM -> combine, over one batch of seeded synthetic tokens with all
+inputs already resident in HBM.  Headline workload: the DeepSeek-V3-shaped prefill batch
+(T=8192, H=7168, 256 experts, top-8 of 8 groups keeping 4, expert and shared intermediate 2048,
+bf16, Zipf-skewed expert load).  The decode batch (T=64, same layer) is reported beside it.
+
+Prints ONE JSON line: throughput (tokens/s), the dominant kernel's roofline (measured with HIP
+events around that kernel inside the timed steps), and the CPU oracle's throughput on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MoE-layer tokens/sec (DeepSeek-V3 shape, bf16) + % HBM/MFMA peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles created through the HIP runtime (timing enabled)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = ev
+        self.n = n
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        self.hip.hipEventSynchronize(self.arr[j])
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def layer_bytes(w, n_hit: int) -> float:
+    """Algorithmic HBM bytes of one layer call: weights of the experts hit, shared expert,
+    router, x and y."""
+    import synth
+    act = synth.act_bytes(w)
+    return (n_hit * synth.expert_bytes(w) + 3 * w.Is * w.H * act + w.E * w.H * act + 2 * w.T * w.H * act)
+
+
+def gemm1_bytes(w, n_hit: int) -> float:
+    """Algorithmic bytes of the gate/up GEMM: gate+up weights of the experts hit and of the
+    shared expert, plus x."""
+    import synth
+    act = synth.act_bytes(w)
+    per_expert = synth.expert_bytes(w) * 2 / 3
+    return n_hit * per_expert + 2 * w.Is * w.H * act + w.T * w.H * act
+
+
+def gemm1_flops(w) -> float:
+    return 4.0 * w.H * (w.I * w.T * w.K + w.Is * w.T)
+
+
+def layer_flops(w) -> float:
+    return 2.0 * w.T * w.H * w.E + 6.0 * w.H * w.I * w.T * w.K + 6.0 * w.H * w.Is * w.T
+
+
+def run_workload(name: str, steps: int, warmup: int, cache: dict):
+    import numpy as np
+    import torch
+
+    import synth
+    import deepseek_gate_expert_amd as dg
+    from deepseek_gate_expert_amd.tensors import DeviceLayer, make_desc, to_device
+
+    w = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    wkey = (w.H, w.E, w.I, w.Is, w.act, w.expert, w.wseed)
+    if wkey not in cache:
+        t0 = time.time()
+        router, experts, shared = synth.gen_router(w), synth.gen_expert_weights(w), synth.gen_shared(w)
+        log(f"[bench] generated {w.expert} weights in {time.time() - t0:.1f}s")
+        t0 = time.time()
+        dev_w = (to_device(router, dev), {k: to_device(v, dev) for k, v in experts.items()},
+                 {k: to_device(v, dev) for k, v in shared.items()})
+        torch.cuda.synchronize()
+        log(f"[bench] uploaded weights in {time.time() - t0:.1f}s")
+        cache.clear()
+        cache[wkey] = ((router, experts, shared), dev_w)
+    (router, experts, shared), (r_d, ex_d, sh_d) = cache[wkey]
+    bias = synth.gen_bias(w)
+    x = synth.gen_x(w, router, bias)
+    offset = synth.gen_logit_offset(w)
+    layer = DeviceLayer(make_desc(w), r_d, to_device(np.ascontiguousarray(bias, np.float32), dev), ex_d, sh_d,
+                        None if offset is None else to_device(offset, dev))
+    layer.ensure_workspace()
+    xd = to_device(x, dev)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    inds = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
+    scores = torch.empty((w.T, w.K), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = layer.forward(xd, y, inds, scores)
+        if rc != 0:
+            raise RuntimeError(f"moe_forward failed: {dg.moe_strerror(rc)}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    counts = np.bincount(inds.cpu().numpy().ravel(), minlength=w.E)
+    n_hit = int(np.count_nonzero(counts))
+
+    ev = HipEvents(2 * steps + 2)
+    assert dg.moe_set_stage_events(dg.MOE_STAGE_GEMM1, ev.arr, steps) == 0
+    try:
+        torch.cuda.synchronize()
+        hip = ev.hip
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventRecord(ev.arr[2 * steps], ctypes.c_void_p(stream.cuda_stream))
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        hip.hipEventRecord(ev.arr[2 * steps + 1], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        step_ms = ev.elapsed_ms(2 * steps, 2 * steps + 1) / steps
+        g1_ms = sum(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)) / steps
+    finally:
+        dg.moe_set_stage_events(-1, None, 0)
+        ev.close()
+    log(f"[bench] {name}: {step_ms:.3f} ms/step (wall {wall_ms:.3f}), gemm1 {g1_ms:.3f} ms, experts hit {n_hit}, "
+        f"max load {counts.max()}")
+    return dict(w=w, step_ms=step_ms, wall_ms=wall_ms, gemm1_ms=g1_ms, n_hit=n_hit, max_load=int(counts.max()),
+                x=x, bias=bias, offset=offset, router=router, experts=experts, shared=shared)
+
+
+def cpu_baseline(res, budget_s: float):
+    """The oracle as it stands on the host cores, on the first n tokens of the same workload
+    (n grown until about `budget_s` seconds of CPU work)."""
+    import oracle
+    w = res["w"]
+    n, spent, rate = 2, 0.0, None
+    while True:
+        rows = list(range(n))
+        t0 = time.perf_counter()
+        oracle.forward_workload(w, res["x"], res["router"], res["bias"], res["experts"], res["shared"],
+                                offset=res["offset"], rows=rows)
+        dt = time.perf_counter() - t0
+        spent += dt
+        rate = n / dt
+        if dt * 2.5 > budget_s or n * 2 > w.T or spent > budget_s:
+            break
+        n *= 2
+    return {"value": rate, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of the {w.name} workload, full layer per token "
+                      f"(router, gate, {w.K} routed + 1 shared SwiGLU expert, combine), fp64 expert math; "
+                      f"{dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3"])
+    ap.add_argument("--no-secondary", action="store_true", help="skip the decode batch")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this layer forward runs on a single MI355X and has no multi-GPU path; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    import torch
+    torch.cuda.init()
+
+    cache = {}
+    main_res = run_workload(args.workload, args.steps, args.warmup, cache)
+    w = main_res["w"]
+    sec = None
+    if not args.no_secondary:
+        other = "c2" if args.workload == "c3" else "c3"
+        sec = run_workload(other, max(args.steps, 20) if other == "c2" else args.steps, args.warmup, cache)
+
+    def summary(res):
+        wl = res["w"]
+        tps = wl.T / (res["step_ms"] / 1e3)
+        decode = wl.T <= 256
+        if decode:
+            ach = gemm1_bytes(wl, res["n_hit"]) / (res["gemm1_ms"] / 1e3) / 1e9
+            roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                    "traffic": None, "kernel": "gemm1_stream (gate/up + SwiGLU)"}
+            layer = layer_bytes(wl, res["n_hit"]) / (res["step_ms"] / 1e3) / 1e9
+            roof["layer_achieved"] = layer
+            roof["layer_frac"] = layer / PEAK_HBM_GBS
+        else:
+            ach = gemm1_flops(wl) / (res["gemm1_ms"] / 1e3) / 1e12
+            roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": "gemm1 (gate/up + SwiGLU)"}
+            layer = layer_flops(wl) / (res["step_ms"] / 1e3) / 1e12
+            roof["layer_achieved"] = layer
+            roof["layer_frac"] = layer / PEAK_BF16_TFLOPS
+        return tps, roof
+
+    tps, roof = summary(main_res)
+    cpu = cpu_baseline(main_res, args.cpu_budget)
+    out = {
+        "metric": METRIC, "value": tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": main_res["step_ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: DeepSeek-V3-shaped {'prefill' if w.T > 256 else 'decode'} batch, "
+                               f"T={w.T} H={w.H} E={w.E} top_k={w.K} n_group={w.G} topk_group={w.TG} "
+                               f"I={w.I} shared I={w.Is}, bf16" + (f", Zipf s={w.zipf_s} expert load"
+                                                                    if w.zipf_s else ""),
+                   "global_batch": w.T, "experts_hit": main_res["n_hit"], "max_expert_load": main_res["max_load"],
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if sec is not None:
+        stps, sroof = summary(sec)
+        sw = sec["w"]
+        out["secondary"] = {"workload": f"{sw.name}: T={sw.T} (same layer)", "value": stps, "unit": "tokens/s",
+                            "ms_per_step": sec["step_ms"], "experts_hit": sec["n_hit"], "roofline": sroof}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

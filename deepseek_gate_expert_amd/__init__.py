@@ -1,0 +1,225 @@
+"""MI355X (gfx950) DeepSeek-style mixture-of-experts layer forward.
+
+Thin ctypes binding of ``libdsmoe.so`` (hand-written HIP, built by ``build.py``).  The names
+and arguments mirror the C ABI in ``include/dsmoe.h``; this module only checks tensor
+properties (device, dtype, shape, contiguity) and passes device pointers, sizes and the current
+HIP stream.  Every step of the layer runs in the library's kernels; there is no fallback: if
+the library is missing, importing the functions works but calling them raises.
+
+Tensor conventions: torch tensors on a ROCm device; bf16 data as ``torch.bfloat16``; 4-bit
+expert weights as ``torch.int32``/``torch.uint32`` words with bf16 scales and offsets.
+Return values are the library's codes (``MOE_OK`` == 0), never exceptions, so the
+validation matrix can be tested as the pages test it (rejects return -1 and leave the outputs
+untouched).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsmoe.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_HIP, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_Q4G64 = 0, 1, 2
+MOE_MAX_EXPERTS, MOE_MAX_TOP_K = 1024, 64
+MOE_STAGE_ROUTER, MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = range(6)
+EXPORTS = ("moe_router_logits", "moe_route_deepseek", "moe_dispatch_workspace_size", "moe_dispatch",
+           "moe_forward_workspace_size", "moe_forward", "moe_set_stage_events", "moe_strerror")
+
+
+class RouteParams(ctypes.Structure):
+    _fields_ = [("top_k", ctypes.c_int32), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("norm_topk_prob", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("I_shared", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
+                ("route", RouteParams)]
+
+
+class ExpertWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_gate", "w_up", "w_down", "s_gate", "b_gate", "s_up", "b_up", "s_down", "b_down")]
+
+
+class SharedWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_up", "w_down")]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdsmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m deepseek_gate_expert_amd.build`")
+        lib = ctypes.CDLL(path)
+        p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.moe_strerror.restype = ctypes.c_char_p
+        lib.moe_strerror.argtypes = [ctypes.c_int]
+        lib.moe_router_logits.restype = ctypes.c_int
+        lib.moe_router_logits.argtypes = [p, p, i32, i64, i32, i32, p, p, p]
+        lib.moe_route_deepseek.restype = ctypes.c_int
+        lib.moe_route_deepseek.argtypes = [p, i64, i32, p, i64, ctypes.POINTER(RouteParams), p, p, p]
+        lib.moe_dispatch_workspace_size.restype = sz
+        lib.moe_dispatch_workspace_size.argtypes = [i64, i32, i32]
+        lib.moe_dispatch.restype = ctypes.c_int
+        lib.moe_dispatch.argtypes = [p, i64, i32, i32, p, p, p, p, p, sz, p]
+        lib.moe_forward_workspace_size.restype = sz
+        lib.moe_forward_workspace_size.argtypes = [ctypes.POINTER(LayerDesc)]
+        lib.moe_forward.restype = ctypes.c_int
+        lib.moe_forward.argtypes = [ctypes.POINTER(LayerDesc), p, p, p, p, ctypes.POINTER(ExpertWeights),
+                                    ctypes.POINTER(SharedWeights), p, p, p, p, sz, p]
+        lib.moe_set_stage_events.restype = ctypes.c_int
+        lib.moe_set_stage_events.argtypes = [i32, p, i32]
+        _lib = lib
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else (t.data_ptr() or None)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream or None
+
+
+def _is_dev(t) -> bool:
+    return t is None or t.is_cuda
+
+
+def _same_device(*ts) -> bool:
+    devs = {t.device for t in ts if t is not None}
+    return len(devs) <= 1 and all(_is_dev(t) for t in ts)
+
+
+def _contig(*ts) -> bool:
+    return all(t is None or t.is_contiguous() for t in ts)
+
+
+def act_code(dtype) -> int:
+    import torch
+    if dtype == torch.float32:
+        return MOE_F32
+    if dtype == torch.bfloat16:
+        return MOE_BF16
+    raise ValueError(f"unsupported activation dtype {dtype}")
+
+
+def route_params(top_k, n_group=1, topk_group=1, norm_topk_prob=True, routed_scaling_factor=1.0) -> RouteParams:
+    return RouteParams(int(top_k), int(n_group), int(topk_group), int(bool(norm_topk_prob)),
+                       float(routed_scaling_factor))
+
+
+def moe_strerror(code: int) -> str:
+    return load_library().moe_strerror(int(code)).decode()
+
+
+def moe_router_logits(x, router_w, logits, logit_offset=None, stream=None) -> int:
+    """logits[T, E] (fp32) = x[T, H] @ router_w[E, H]^T (+ logit_offset[E]), fixed fp32 order."""
+    import torch
+    if x.dim() != 2 or router_w.dim() != 2 or logits.dim() != 2 or logits.dtype != torch.float32:
+        return MOE_ERR_INVALID
+    if x.dtype != router_w.dtype or not _same_device(x, router_w, logits, logit_offset) or \
+            not _contig(x, router_w, logits, logit_offset):
+        return MOE_ERR_INVALID
+    T, H = x.shape
+    E = router_w.shape[0]
+    if router_w.shape[1] != H or tuple(logits.shape) != (T, E):
+        return MOE_ERR_INVALID
+    if logit_offset is not None and (logit_offset.dtype != torch.float32 or tuple(logit_offset.shape) != (E,)):
+        return MOE_ERR_INVALID
+    return load_library().moe_router_logits(_ptr(x), _ptr(router_w), act_code(x.dtype), T, H, E,
+                                            _ptr(logit_offset), _ptr(logits), _stream(stream))
+
+
+def moe_route_deepseek(logits, bias, inds, scores, top_k, n_group=1, topk_group=1, norm_topk_prob=True,
+                       routed_scaling_factor=1.0, stream=None) -> int:
+    """DeepSeek gate on logits [..., E] (leading dims flatten to rows).  inds (int32) and
+    scores (fp32) are [..., top_k] and are written only on success."""
+    import torch
+    if logits.dim() < 1 or logits.dtype != torch.float32:
+        return MOE_ERR_INVALID
+    # the reviewed contract: bias is rank-1 [E], fp32, on the logits' device
+    if bias is None or bias.dim() != 1 or bias.dtype != torch.float32:
+        return MOE_ERR_INVALID
+    if inds.dtype != torch.int32 or scores.dtype != torch.float32:
+        return MOE_ERR_INVALID
+    if not _same_device(logits, bias, inds, scores) or not _contig(logits, bias, inds, scores):
+        return MOE_ERR_INVALID
+    E = logits.shape[-1]
+    T = logits.numel() // E if E > 0 else 0
+    if inds.numel() != T * max(int(top_k), 0) or scores.numel() != inds.numel():
+        return MOE_ERR_INVALID
+    p = route_params(top_k, n_group, topk_group, norm_topk_prob, routed_scaling_factor)
+    return load_library().moe_route_deepseek(_ptr(logits), T, E, _ptr(bias), bias.shape[0], ctypes.byref(p),
+                                             _ptr(inds), _ptr(scores), _stream(stream))
+
+
+def moe_dispatch_workspace_size(T: int, K: int, E: int) -> int:
+    return int(load_library().moe_dispatch_workspace_size(T, K, E))
+
+
+def moe_dispatch(inds, E, counts, offsets, sorted_slot, slot_row, workspace, stream=None) -> int:
+    """Stable counting sort of the T*K slots of inds [T, K] by expert (see dsmoe.h)."""
+    import torch
+    ts = (inds, counts, offsets, sorted_slot, slot_row)
+    if any(t.dtype != torch.int32 for t in ts) or inds.dim() != 2:
+        return MOE_ERR_INVALID
+    if not _same_device(*ts, workspace) or not _contig(*ts):
+        return MOE_ERR_INVALID
+    T, K = inds.shape
+    if counts.numel() != E or offsets.numel() != E + 1 or sorted_slot.numel() != T * K or slot_row.numel() != T * K:
+        return MOE_ERR_INVALID
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return load_library().moe_dispatch(_ptr(inds), T, K, E, _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
+                                       _ptr(slot_row), _ptr(workspace), nbytes, _stream(stream))
+
+
+def layer_desc(T, H, E, I, I_shared, act_dtype, expert_dtype, top_k, n_group=1, topk_group=1, norm_topk_prob=True,
+               routed_scaling_factor=1.0) -> LayerDesc:
+    return LayerDesc(int(T), int(H), int(E), int(I), int(I_shared), int(act_dtype), int(expert_dtype),
+                     route_params(top_k, n_group, topk_group, norm_topk_prob, routed_scaling_factor))
+
+
+def moe_forward_workspace_size(desc: LayerDesc) -> int:
+    return int(load_library().moe_forward_workspace_size(ctypes.byref(desc)))
+
+
+def moe_forward(desc: LayerDesc, x, router_w, bias, experts: dict, shared: Optional[dict], y, logit_offset=None,
+                inds_out=None, scores_out=None, workspace=None, stream=None) -> int:
+    """Whole MoE layer forward (see dsmoe.h).  experts: dict with 'gate', 'up', 'down' (and for
+    4-bit weights 's_gate', 'b_gate', 's_up', 'b_up', 's_down', 'b_down'); shared: dict with
+    'gate', 'up', 'down' or None."""
+    import torch
+    if not _contig(x, router_w, bias, y, logit_offset, inds_out, scores_out, workspace):
+        return MOE_ERR_INVALID
+    if bias.dim() != 1 or bias.dtype != torch.float32:
+        return MOE_ERR_INVALID
+    ew = ExpertWeights(*[_ptr(experts.get(k)) for k in
+                         ("gate", "up", "down", "s_gate", "b_gate", "s_up", "b_up", "s_down", "b_down")])
+    sw = None
+    if shared is not None:
+        sw = SharedWeights(_ptr(shared["gate"]), _ptr(shared["up"]), _ptr(shared["down"]))
+    tensors = [x, router_w, bias, y, logit_offset, inds_out, scores_out, workspace] + \
+        [v for v in experts.values()] + ([] if shared is None else list(shared.values()))
+    if not _same_device(*tensors):
+        return MOE_ERR_INVALID
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return load_library().moe_forward(ctypes.byref(desc), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(logit_offset),
+                                      ctypes.byref(ew), None if sw is None else ctypes.byref(sw), _ptr(y),
+                                      _ptr(inds_out), _ptr(scores_out), _ptr(workspace), nbytes, _stream(stream))
+
+
+def moe_set_stage_events(stage: int, events, n_pairs: int) -> int:
+    """Measurement hook (see dsmoe.h): `events` is a ctypes array of 2*n_pairs hipEvent_t
+    handles; stage -1 clears."""
+    return load_library().moe_set_stage_events(int(stage), events, int(n_pairs))

@@ -1,0 +1,294 @@
+// api.hip - the C ABI of libdsmoe: host-side validation, workspace layout and the launch
+// sequence of the MoE layer forward.  Contract and citations: include/dsmoe.h.
+//
+// Everything here is host code.  All argument checks run before the first HIP call, so a
+// rejected call touches no device memory.  No call synchronises the stream or reads device
+// memory back; expert counts stay on the device and the expert kernels read them there.
+#include <stdint.h>
+#include <string.h>
+
+#include "dsmoe_internal.hpp"
+
+using namespace dsmoe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+inline size_t up(size_t v) { return (v + ALIGN - 1) & ~(ALIGN - 1); }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// pointer may be NULL only when `may_be_null`
+inline bool ptr_ok(const void* p, bool may_be_null) { return p ? aligned16(p) : may_be_null; }
+
+int check_route_params(int32_t E, const moe_route_params* p) {
+    if (!p) return MOE_ERR_INVALID;
+    if (E < 1) return MOE_ERR_INVALID;
+    if (p->top_k < 1 || p->top_k > E) return MOE_ERR_INVALID;
+    if (p->n_group < 1 || E % p->n_group != 0) return MOE_ERR_INVALID;
+    if (p->topk_group < 1 || p->topk_group > p->n_group) return MOE_ERR_INVALID;
+    if (p->n_group > 1 && E / p->n_group < 2) return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || p->top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+size_t dispatch_ws_bytes(int64_t T, int32_t K, int32_t E) {
+    return up((size_t)dispatch_blocks(T * K) * (size_t)E * sizeof(int32_t));
+}
+
+struct FwdLayout {
+    size_t logits, inds, scores, blk, counts, offsets, sorted_slot, slot_row, h, o, total;
+};
+
+FwdLayout fwd_layout(const moe_layer_desc* d) {
+    FwdLayout L;
+    const size_t T = (size_t)d->T, K = (size_t)d->route.top_k, E = (size_t)d->E;
+    const size_t TK = T * K;
+    const size_t rows = TK + (d->I_shared > 0 ? T : 0);
+    const size_t el = d->act_dtype == MOE_F32 ? 4 : 2;
+    const size_t ldh = (size_t)(d->I > d->I_shared ? d->I : d->I_shared);
+    size_t off = 0;
+    L.logits = off;
+    off += up(T * E * 4);
+    L.inds = off;
+    off += up(TK * 4);
+    L.scores = off;
+    off += up(TK * 4);
+    L.blk = off;
+    off += dispatch_ws_bytes(d->T, d->route.top_k, d->E);
+    L.counts = off;
+    off += up(E * 4);
+    L.offsets = off;
+    off += up((E + 1) * 4);
+    L.sorted_slot = off;
+    off += up(TK * 4);
+    L.slot_row = off;
+    off += up(TK * 4);
+    L.h = off;
+    off += up(rows * ldh * el);
+    L.o = off;
+    off += up(rows * (size_t)d->H * el);
+    L.total = off;
+    return L;
+}
+
+int check_desc(const moe_layer_desc* d) {
+    if (!d) return MOE_ERR_INVALID;
+    if (d->T < 0 || d->H < 1 || d->E < 1 || d->I < 1 || d->I_shared < 0) return MOE_ERR_INVALID;
+    const int32_t a = d->act_dtype, w = d->expert_dtype;
+    const bool combo = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_Q4G64));
+    if (!combo) return MOE_ERR_INVALID;
+    int rc = check_route_params(d->E, &d->route);
+    if (rc != MOE_OK) return rc;
+    if ((int64_t)d->T * (d->route.top_k + 1) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (a == MOE_BF16 && (d->H % 64 || d->I % 64 || d->I_shared % 64)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// measurement hook state (see moe_set_stage_events)
+struct StageHook {
+    int32_t stage = -1;
+    hipEvent_t const* events = nullptr;
+    int32_t n_pairs = 0;
+    int64_t calls = 0;
+};
+StageHook g_hook;
+
+// records the hook's start (edge 0) or stop (edge 1) event of `stage` for the current call
+inline hipError_t mark(int32_t stage, int edge, hipStream_t s) {
+    if (g_hook.stage != stage || g_hook.n_pairs <= 0) return hipSuccess;
+    const int64_t i = g_hook.calls % g_hook.n_pairs;
+    return hipEventRecord(g_hook.events[2 * i + edge], s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_set_stage_events(int32_t stage, void* const* events, int32_t n_pairs) {
+    if (stage < -1 || stage > MOE_STAGE_COMBINE || n_pairs < 0 || (n_pairs > 0 && !events && stage >= 0))
+        return MOE_ERR_INVALID;
+    g_hook.stage = (stage < 0 || n_pairs == 0) ? -1 : stage;
+    g_hook.events = (hipEvent_t const*)events;
+    g_hook.n_pairs = g_hook.stage < 0 ? 0 : n_pairs;
+    g_hook.calls = 0;
+    return MOE_OK;
+}
+
+const char* moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID: return "invalid argument";
+        case MOE_ERR_HIP: return "HIP launch or runtime error";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_UNSUPPORTED: return "valid but unsupported by this implementation";
+        default: return "unknown error code";
+    }
+}
+
+int moe_router_logits(const void* x, const void* router_w, int32_t act_dtype, int64_t T, int32_t H, int32_t E,
+                      const float* logit_offset, float* logits, void* stream) {
+    if (T < 0 || H < 1 || E < 1) return MOE_ERR_INVALID;
+    if (act_dtype != MOE_F32 && act_dtype != MOE_BF16) return MOE_ERR_INVALID;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr_ok(router_w, false) || !ptr_ok(logits, empty) || !ptr_ok(logit_offset, true))
+        return MOE_ERR_INVALID;
+    if (empty) return MOE_OK;
+    return hip_rc(launch_router(x, router_w, act_dtype, T, H, E, logit_offset, logits, (hipStream_t)stream));
+}
+
+int moe_route_deepseek(const float* logits, int64_t T, int32_t E, const float* bias, int64_t bias_len,
+                       const moe_route_params* p, int32_t* inds, float* scores, void* stream) {
+    if (T < 0) return MOE_ERR_INVALID;
+    const bool empty = T == 0;
+    if (!ptr_ok(logits, empty) || !ptr_ok(bias, false) || !ptr_ok(inds, empty) || !ptr_ok(scores, empty))
+        return MOE_ERR_INVALID;
+    if (bias_len != E) return MOE_ERR_INVALID;
+    const int rc = check_route_params(E, p);
+    if (rc != MOE_OK) return rc;
+    if (empty) return MOE_OK;
+    return hip_rc(launch_route(logits, T, E, bias, *p, inds, scores, (hipStream_t)stream));
+}
+
+size_t moe_dispatch_workspace_size(int64_t T, int32_t K, int32_t E) {
+    if (T < 0 || K < 1 || E < 1 || E > MOE_MAX_EXPERTS || T * K >= ((int64_t)1 << 31)) return 0;
+    return dispatch_ws_bytes(T, K, E);
+}
+
+int moe_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_slot, int32_t* slot_row, void* workspace, size_t workspace_bytes, void* stream) {
+    if (T < 0 || K < 1 || E < 1) return MOE_ERR_INVALID;
+    const bool empty = T == 0;
+    if (!ptr_ok(inds, empty) || !ptr_ok(counts, false) || !ptr_ok(offsets, false) || !ptr_ok(sorted_slot, empty) ||
+        !ptr_ok(slot_row, empty))
+        return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || T * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    const size_t need = dispatch_ws_bytes(T, K, E);
+    if (need > 0 && !ptr_ok(workspace, false)) return MOE_ERR_INVALID;
+    if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    return hip_rc(launch_dispatch(inds, T, K, E, counts, offsets, sorted_slot, slot_row, (int32_t*)workspace,
+                                  (hipStream_t)stream));
+}
+
+size_t moe_forward_workspace_size(const moe_layer_desc* d) {
+    if (check_desc(d) != MOE_OK) return 0;
+    return fwd_layout(d).total;
+}
+
+int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, const float* bias,
+                const float* logit_offset, const moe_expert_weights* ew, const moe_shared_weights* sw, void* y,
+                int32_t* inds_out, float* scores_out, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_desc(d);
+    if (rc != MOE_OK) return rc;
+    const bool empty = d->T == 0;
+    if (!ptr_ok(x, empty) || !ptr_ok(router_w, false) || !ptr_ok(bias, false) || !ptr_ok(logit_offset, true) ||
+        !ptr_ok(y, empty) || !ptr_ok(inds_out, true) || !ptr_ok(scores_out, true))
+        return MOE_ERR_INVALID;
+    if (!ew || !ptr_ok(ew->w_gate, false) || !ptr_ok(ew->w_up, false) || !ptr_ok(ew->w_down, false))
+        return MOE_ERR_INVALID;
+    if (d->expert_dtype == MOE_Q4G64 &&
+        (!ptr_ok(ew->s_gate, false) || !ptr_ok(ew->b_gate, false) || !ptr_ok(ew->s_up, false) ||
+         !ptr_ok(ew->b_up, false) || !ptr_ok(ew->s_down, false) || !ptr_ok(ew->b_down, false)))
+        return MOE_ERR_INVALID;
+    if (d->I_shared > 0) {
+        if (!sw || !ptr_ok(sw->w_gate, false) || !ptr_ok(sw->w_up, false) || !ptr_ok(sw->w_down, false))
+            return MOE_ERR_INVALID;
+    } else if (sw) {
+        return MOE_ERR_INVALID;
+    }
+    const FwdLayout L = fwd_layout(d);
+    if (!ptr_ok(workspace, false) || ((uintptr_t)workspace & (ALIGN - 1))) return MOE_ERR_INVALID;
+    if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (empty) return MOE_OK;
+
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    float* logits = (float*)(ws + L.logits);
+    int32_t* inds = inds_out ? inds_out : (int32_t*)(ws + L.inds);
+    float* scores = scores_out ? scores_out : (float*)(ws + L.scores);
+    int32_t* blk = (int32_t*)(ws + L.blk);
+    int32_t* counts = (int32_t*)(ws + L.counts);
+    int32_t* offsets = (int32_t*)(ws + L.offsets);
+    int32_t* sorted_slot = (int32_t*)(ws + L.sorted_slot);
+    int32_t* slot_row = (int32_t*)(ws + L.slot_row);
+
+    if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 0, s)))) return rc;
+    if ((rc = hip_rc(launch_router(x, router_w, d->act_dtype, d->T, d->H, d->E, logit_offset, logits, s))))
+        return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 1, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_ROUTE, 0, s)))) return rc;
+    if ((rc = hip_rc(launch_route(logits, d->T, d->E, bias, d->route, inds, scores, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_ROUTE, 1, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_DISPATCH, 0, s)))) return rc;
+    if ((rc = hip_rc(launch_dispatch(inds, d->T, d->route.top_k, d->E, counts, offsets, sorted_slot, slot_row, blk,
+                                     s))))
+        return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_DISPATCH, 1, s)))) return rc;
+
+    GroupedArgs a;
+    memset(&a, 0, sizeof(a));
+    a.T = d->T;
+    a.H = d->H;
+    a.E = d->E;
+    a.I = d->I;
+    a.Is = d->I_shared;
+    a.K = d->route.top_k;
+    a.TK = (int32_t)(d->T * d->route.top_k);
+    a.ldh = d->I > d->I_shared ? d->I : d->I_shared;
+    a.offsets = offsets;
+    a.sorted_slot = sorted_slot;
+    a.inds = inds;
+    a.x = x;
+    a.h = ws + L.h;
+    a.o = ws + L.o;
+    a.wg = ew->w_gate;
+    a.wu = ew->w_up;
+    a.wd = ew->w_down;
+    if (d->expert_dtype == MOE_Q4G64) {
+        a.sg = (const bf16_t*)ew->s_gate;
+        a.bg = (const bf16_t*)ew->b_gate;
+        a.su = (const bf16_t*)ew->s_up;
+        a.bu = (const bf16_t*)ew->b_up;
+        a.sd = (const bf16_t*)ew->s_down;
+        a.bd = (const bf16_t*)ew->b_down;
+    }
+    if (d->I_shared > 0) {
+        a.swg = sw->w_gate;
+        a.swu = sw->w_up;
+        a.swd = sw->w_down;
+    }
+
+    const int32_t E = d->E;
+    const int32_t gend = E + (d->I_shared > 0 ? 1 : 0);
+    const bool f32 = d->act_dtype == MOE_F32, q4 = d->expert_dtype == MOE_Q4G64;
+    if ((rc = hip_rc(mark(MOE_STAGE_GEMM1, 0, s)))) return rc;
+    if (f32) {
+        rc = hip_rc(launch_gemm1_f32(a, s));
+    } else if (!q4) {
+        rc = hip_rc(launch_gemm1_bf16(a, 0, gend, MOE_BF16, s));
+    } else {
+        rc = hip_rc(launch_gemm1_bf16(a, 0, E, MOE_Q4G64, s));
+        if (!rc) rc = hip_rc(launch_gemm1_bf16(a, E, gend, MOE_BF16, s));
+    }
+    if (rc || (rc = hip_rc(mark(MOE_STAGE_GEMM1, 1, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_GEMM2, 0, s)))) return rc;
+    if (f32) {
+        rc = hip_rc(launch_gemm2_f32(a, s));
+    } else if (!q4) {
+        rc = hip_rc(launch_gemm2_bf16(a, 0, gend, MOE_BF16, s));
+    } else {
+        rc = hip_rc(launch_gemm2_bf16(a, 0, E, MOE_Q4G64, s));
+        if (!rc) rc = hip_rc(launch_gemm2_bf16(a, E, gend, MOE_BF16, s));
+    }
+    if (rc || (rc = hip_rc(mark(MOE_STAGE_GEMM2, 1, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 0, s)))) return rc;
+    if ((rc = hip_rc(launch_combine(a, d->act_dtype, scores, slot_row, y, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 1, s)))) return rc;
+    ++g_hook.calls;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// dsmoe_internal.hpp - device helpers and kernel launchers of libdsmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsmoe.h"
+
+namespace dsmoe {
+
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+static_assert(sizeof(bf16x8) == 16, "bf16x8 is 16 bytes");
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(bf16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// One launch of the grouped expert GEMMs.  Groups g in [0, E) are the routed experts with
+// rows [offsets[g], offsets[g+1]) of the expert-major row space; group E is the shared expert
+// with rows [TK, TK + T) (row TK + t is token t).
+struct GroupedArgs {
+    int64_t T;
+    int32_t H, E, I, Is, K;      // K = top_k
+    int32_t TK;                  // T * K
+    int32_t ldh;                 // row stride of h (max(I, Is))
+    const int32_t* offsets;      // [E + 1]
+    const int32_t* sorted_slot;  // [TK]
+    const int32_t* inds;         // [T, K]
+    const void* x;               // [T, H] act
+    void* h;                     // [TK + T, ldh] act (SwiGLU intermediate)
+    void* o;                     // [TK + T, H] act (per-row expert output)
+    const void* wg;              // routed [E, I, H] (q4: uint32 [E, I, H/8])
+    const void* wu;
+    const void* wd;              // routed [E, H, I]
+    const bf16_t *sg, *bg, *su, *bu, *sd, *bd;  // q4 scale / offset [E, out, in/64]
+    const void* swg;             // shared [Is, H] act
+    const void* swu;
+    const void* swd;             // shared [H, Is] act
+};
+
+// launchers (return hipSuccess or the launch error)
+hipError_t launch_router(const void* x, const void* w, int32_t act, int64_t T, int32_t H, int32_t E,
+                         const float* offset, float* logits, hipStream_t s);
+hipError_t launch_route(const float* logits, int64_t T, int32_t E, const float* bias, const moe_route_params& p,
+                        int32_t* inds, float* scores, hipStream_t s);
+int32_t dispatch_blocks(int64_t TK);
+hipError_t launch_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_slot, int32_t* slot_row, int32_t* blk, hipStream_t s);
+// bf16-activation expert GEMMs for groups [g0, g1); wdt = weight dtype of those groups
+// (MOE_BF16 or MOE_Q4G64; the shared group E is always bf16)
+hipError_t launch_gemm1_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s);
+hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s);
+// fp32 layers: all routed rows and the shared rows in one launch each
+hipError_t launch_gemm1_f32(const GroupedArgs& a, hipStream_t s);
+hipError_t launch_gemm2_f32(const GroupedArgs& a, hipStream_t s);
+hipError_t launch_combine(const GroupedArgs& a, int32_t act, const float* scores, const int32_t* slot_row,
+                          void* y, hipStream_t s);
+
+}  // namespace dsmoe

@@ -77,8 +77,14 @@ def _L():
         lib.oracle_swiglu.argtypes = [p, i32, i32, i32] + [p] * 9 + [p]
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_forward.argtypes = [ctypes.POINTER(Layer), p, i64, p, p, p, p]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    return int(_L().oracle_num_threads())
 
 
 def lib_path() -> str:
@@ -185,3 +191,18 @@ def forward_workload(w, x, router_w, bias, experts, shared, offset=None, rows=No
     """`forward` with the shape/route parameters taken from a synth.Workload."""
     return forward(x, router_w, bias, experts, shared, T=w.T, H=w.H, E=w.E, I=w.I, Is=w.Is, K=w.K, G=w.G,
                    TG=w.TG, norm=w.norm, rsf=w.rsf, act=w.act, expert=w.expert, offset=offset, rows=rows)
+
+
+def dispatch(inds: np.ndarray, E: int):
+    """Expert-major grouping of the T*K token slots (slot s = t*K + j), the grouping that the
+    gather_mm / gather_qmm expert calls imply ("Epic: Engine Inference Core Stage E - MoE +
+    hybrid families", opening paragraph): experts ascending, slots ascending inside an expert.
+    Returns (counts [E], offsets [E+1], sorted_slot [T*K], slot_row [T*K]); a stable sort
+    (library primitive) is the definition."""
+    flat = np.asarray(inds).ravel().astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    sorted_slot = np.argsort(flat, kind="stable").astype(np.int32)
+    slot_row = np.empty_like(sorted_slot)
+    slot_row[sorted_slot] = np.arange(len(flat), dtype=np.int32)
+    return counts, offsets, sorted_slot, slot_row

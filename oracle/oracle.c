@@ -329,3 +329,15 @@ int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, d
     free(o);
     return 0;
 }
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+/* number of host threads the OpenMP loops above use */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

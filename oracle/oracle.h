@@ -83,6 +83,9 @@ void oracle_swiglu(const double* x, int32_t H, int32_t I, int32_t dtype, const v
 int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, double* y, int32_t* inds,
                    float* scores, float* logits);
 
+/* host threads used by the OpenMP loops */
+int oracle_num_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

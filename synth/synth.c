@@ -67,20 +67,48 @@ static inline float bf16_to_f32(uint16_t h) {
     return f;
 }
 
+/* both normals of pair p (elements 2p and 2p+1); same values as normal_at */
+static inline void normal_pair(uint64_t key, uint64_t p, double* z0, double* z1) {
+    uint64_t a = bits_at(key, 2 * p), b = bits_at(key, 2 * p + 1);
+    double u1 = ((double)(a >> 11) + 0.5) * 0x1.0p-53;
+    double u2 = (double)(b >> 11) * 0x1.0p-53;
+    double r = sqrt(-2.0 * log(u1));
+    double t = 6.283185307179586476925286766559 * u2;
+    *z0 = r * cos(t);
+    *z1 = r * sin(t);
+}
+
 /* out[j] = float(std * N(0,1) element (start+j)) + mean */
 void synth_normal_f32(uint64_t seed, uint64_t tid, uint64_t start, int64_t n, double mean, double std,
                       float* out) {
     uint64_t key = key_of(seed, tid);
+    if (n <= 0) return;
+    uint64_t p0 = start >> 1, p1 = (start + (uint64_t)n - 1) >> 1;
 #pragma omp parallel for schedule(static)
-    for (int64_t j = 0; j < n; ++j) out[j] = (float)(mean + std * normal_at(key, start + (uint64_t)j));
+    for (int64_t q = 0; q <= (int64_t)(p1 - p0); ++q) {
+        uint64_t p = p0 + (uint64_t)q;
+        double z0, z1;
+        normal_pair(key, p, &z0, &z1);
+        int64_t j0 = (int64_t)(2 * p) - (int64_t)start;
+        if (j0 >= 0 && j0 < n) out[j0] = (float)(mean + std * z0);
+        if (j0 + 1 >= 0 && j0 + 1 < n) out[j0 + 1] = (float)(mean + std * z1);
+    }
 }
 
 void synth_normal_bf16(uint64_t seed, uint64_t tid, uint64_t start, int64_t n, double mean, double std,
                        uint16_t* out) {
     uint64_t key = key_of(seed, tid);
+    if (n <= 0) return;
+    uint64_t p0 = start >> 1, p1 = (start + (uint64_t)n - 1) >> 1;
 #pragma omp parallel for schedule(static)
-    for (int64_t j = 0; j < n; ++j)
-        out[j] = f32_to_bf16_rne((float)(mean + std * normal_at(key, start + (uint64_t)j)));
+    for (int64_t q = 0; q <= (int64_t)(p1 - p0); ++q) {
+        uint64_t p = p0 + (uint64_t)q;
+        double z0, z1;
+        normal_pair(key, p, &z0, &z1);
+        int64_t j0 = (int64_t)(2 * p) - (int64_t)start;
+        if (j0 >= 0 && j0 < n) out[j0] = f32_to_bf16_rne((float)(mean + std * z0));
+        if (j0 + 1 >= 0 && j0 + 1 < n) out[j0 + 1] = f32_to_bf16_rne((float)(mean + std * z1));
+    }
 }
 
 /* fp32 -> bf16 (RNE) conversion of an existing buffer */
@@ -104,8 +132,13 @@ void synth_q4_normal(uint64_t seed, uint64_t tid, uint64_t start, int64_t rows, 
         float w[64];
         uint64_t base = start + (uint64_t)(r * cols + g * 64);
         float mn = INFINITY, mx = -INFINITY;
+        for (int i = 0; i < 64; i += 2) {
+            double z0, z1; /* base is even: elements base+i, base+i+1 form one pair */
+            normal_pair(key, (base + (uint64_t)i) >> 1, &z0, &z1);
+            w[i] = (float)(std * z0);
+            w[i + 1] = (float)(std * z1);
+        }
         for (int i = 0; i < 64; ++i) {
-            w[i] = (float)(std * normal_at(key, base + (uint64_t)i));
             if (w[i] < mn) mn = w[i];
             if (w[i] > mx) mx = w[i];
         }

@@ -1,0 +1,171 @@
+"""GPU parity of the whole layer (moe_forward) against the oracle.
+
+Pages: "Epic: Engine Inference Core Stage E - MoE + hybrid families" (gather_mm / gather_qmm
+expert dispatch, shared experts always active) and the gate page's merge recommendation
+(router -> route -> switch_glu -> combine).  Bar: routing indices bit-exact, gate weights
+within relative 1e-6, y within relative L2 1e-5 (fp32 layers), 1e-2 (bf16) and 2e-2 (4-bit),
+against the oracle's fp64 expert math.  The five workloads run at full size; for the two
+largest the oracle computes y on a sample of tokens (its routing covers every token).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import deepseek_gate_expert_amd as dg
+from deepseek_gate_expert_amd.tensors import to_device, upload_layer
+from _gpu import DEV, Case, act_to_f64, log, rel_l2, tol_of
+
+pytestmark = pytest.mark.gpu
+
+
+def check_route(gi, gs, oi, os_):
+    bad = np.nonzero(np.any(gi != oi, axis=1))[0]
+    assert len(bad) == 0, f"{len(bad)} token rows routed differently, first {bad[:4]}"
+    den = np.maximum(np.abs(os_.astype(np.float64)), 1e-30)
+    assert np.max(np.abs(gs.astype(np.float64) - os_) / den) <= 1e-6
+
+
+@pytest.mark.parametrize("name", ["c0", "c1", "c2"])
+def test_layer_full(name):
+    w = synth.WORKLOADS[name]
+    log(f"[layer] {w.desc}")
+    c = Case(w)
+    y, inds, scores = c.gpu()
+    y_ref, oi, os_, _ = c.oracle_rows()
+    check_route(inds.cpu().numpy(), scores.cpu().numpy(), oi, os_)
+    err = rel_l2(act_to_f64(y), y_ref)
+    log(f"[layer] {name} rel L2 {err:.3e}")
+    assert err <= tol_of(w)
+
+
+@pytest.mark.parametrize("name,n_sample", [("c3", 24), ("c4", 24)])
+def test_layer_full_size_sampled(name, n_sample):
+    w = synth.WORKLOADS[name]
+    log(f"[layer] {w.desc} (sampled)")
+    c = Case(w)
+    y, inds, scores = c.gpu()
+    _, oi, os_ = c.oracle_route_all()
+    check_route(inds.cpu().numpy(), scores.cpu().numpy(), oi, os_)
+    # sample: evenly spread tokens plus tokens routed to the most and least loaded experts
+    counts = np.bincount(oi.ravel(), minlength=w.E)
+    hot, cold = int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    rows = set(np.linspace(0, w.T - 1, n_sample - 4).astype(int).tolist())
+    rows |= set(np.nonzero(np.any(oi == hot, axis=1))[0][:2].tolist())
+    rows |= set(np.nonzero(np.any(oi == cold, axis=1))[0][:2].tolist())
+    rows = sorted(rows)
+    y_ref, _, _, _ = c.oracle_rows(rows)
+    err = rel_l2(act_to_f64(y)[rows], y_ref)
+    log(f"[layer] {name} sampled rel L2 {err:.3e}; experts hit {int(np.count_nonzero(counts))}, max load {counts.max()}")
+    assert err <= tol_of(w)
+
+
+def small_case(w, seed_shift=0):
+    w = w.with_(seed=w.seed + seed_shift)
+    r = synth.gen_router(w)
+    b = synth.gen_bias(w)
+    x = synth.gen_x(w, r, b)
+    ex = synth.gen_expert_weights(w)
+    sh = synth.gen_shared(w)
+    off = synth.gen_logit_offset(w)
+    return w, r, b, x, ex, sh, off
+
+
+def run_small(w, r, b, x, ex, sh, off):
+    layer = upload_layer(w, r, b, ex, sh if w.Is > 0 else None, off, DEV)
+    y, inds, scores = layer(to_device(x, DEV), want_route=True)
+    torch.cuda.synchronize()
+    return y, inds.cpu().numpy(), scores.cpu().numpy()
+
+
+C1 = synth.WORKLOADS["c1"]
+EDGE = [
+    ("T1", C1.with_(T=1, planted=0)),
+    ("ragged_T", C1.with_(T=37, planted=0)),
+    ("top_k_1", C1.with_(T=64, K=1, planted=0)),
+    ("no_dropped_group", C1.with_(T=64, TG=4, planted=0)),
+    ("K_above_kept", C1.with_(T=32, K=40, G=8, TG=2, planted=0)),
+    ("no_shared", C1.with_(T=48, Is=0, planted=0)),
+    ("shared_narrower", C1.with_(T=48, I=256, Is=128, planted=0)),
+    ("shared_wider", C1.with_(T=48, I=128, Is=320, planted=0)),
+    ("H_tail_64", C1.with_(T=40, H=192, I=192, Is=64, planted=0)),
+    ("q4_small", C1.with_(T=50, expert="q4", planted=0)),
+    ("q4_tail", C1.with_(T=20, H=320, I=192, Is=192, expert="q4", planted=0)),
+    ("f32_ragged", synth.WORKLOADS["c0"].with_(T=21, H=40, I=24, Is=12)),
+    ("f32_groups", synth.WORKLOADS["c0"].with_(T=30, E=16, K=4, G=4, TG=2, H=72)),
+    ("zipf_skew", C1.with_(T=400, zipf_s=3.0, planted=0)),
+    ("dsv3_decode_small_batch", synth.WORKLOADS["c2"].with_(T=3, H=512, I=256, Is=256)),
+]
+
+
+@pytest.mark.parametrize("label,w", EDGE, ids=[e[0] for e in EDGE])
+def test_layer_edge_cases(label, w):
+    log(f"[edge] {label}: {w.desc}")
+    args = small_case(w)
+    y, gi, gs = run_small(*args)
+    w_, r, b, x, ex, sh, off = args
+    y_ref, oi, os_, _ = oracle.forward_workload(w_, x, r, b, ex, sh if w_.Is > 0 else None, offset=off)
+    check_route(gi, gs, oi, os_)
+    err = rel_l2(act_to_f64(y), y_ref)
+    log(f"[edge] {label} rel L2 {err:.3e}")
+    assert err <= tol_of(args[0])
+
+
+def test_layer_one_hot_expert_load():
+    """Every token picks the same top expert (a large bias): that expert's group holds all T rows,
+    which exercises the row-chunk loop of the expert kernels."""
+    w = C1.with_(T=300, K=2, planted=0)
+    w_, r, b, x, ex, sh, off = small_case(w)
+    b = b.copy()
+    b[5] = 50.0
+    y, gi, gs = run_small(w_, r, b, x, ex, sh, off)
+    assert np.all(gi[:, 0] == 5)
+    y_ref, oi, os_, _ = oracle.forward_workload(w_, x, r, b, ex, sh)
+    check_route(gi, gs, oi, os_)
+    assert rel_l2(act_to_f64(y), y_ref) <= 1e-2
+
+
+def test_layer_zero_tokens_and_deterministic():
+    w = C1.with_(T=64, planted=0)
+    w_, r, b, x, ex, sh, off = small_case(w)
+    layer = upload_layer(w_, r, b, ex, sh, off, DEV)
+    xd = to_device(x, DEV)
+    y1 = layer(xd)
+    y2 = layer(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # T = 0 is a no-op that returns OK
+    desc0 = dg.layer_desc(0, w.H, w.E, w.I, w.Is, dg.MOE_BF16, dg.MOE_BF16, w.K, w.G, w.TG, w.norm, w.rsf)
+    ws = layer.ensure_workspace()
+    y0 = torch.empty((0, w.H), dtype=torch.bfloat16, device=DEV)
+    assert dg.moe_forward(desc0, xd[:0], layer.router, layer.bias, layer.experts, layer.shared, y0, workspace=ws) == 0
+
+
+def test_layer_rejects_leave_output_untouched():
+    w = C1.with_(T=16, planted=0)
+    w_, r, b, x, ex, sh, off = small_case(w)
+    layer = upload_layer(w_, r, b, ex, sh, off, DEV)
+    xd = to_device(x, DEV)
+    y = torch.full((w.T, w.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    ws = layer.ensure_workspace()
+    bad = dg.layer_desc(w.T, w.H, w.E, w.I, w.Is, dg.MOE_BF16, dg.MOE_BF16, w.K, 3, 1, True, 2.5)  # 64 % 3 != 0
+    assert dg.moe_forward(bad, xd, layer.router, layer.bias, layer.experts, layer.shared, y, workspace=ws) == -1
+    small = ws[: ws.numel() // 2]
+    assert dg.moe_forward(layer.desc, xd, layer.router, layer.bias, layer.experts, layer.shared, y,
+                          workspace=small) == dg.MOE_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
+
+
+def test_layer_bias_changes_selection_not_weights():
+    """S1 at layer level: raising one expert's bias moves it into every token's selection; its
+    weight is still its pre-bias sigmoid share."""
+    w = C1.with_(T=32, G=1, TG=1, K=2, norm=False, rsf=1.0, planted=0)
+    w_, r, b, x, ex, sh, off = small_case(w)
+    b2 = b.copy()
+    b2[9] = 10.0
+    _, gi, gs = run_small(w_, r, b2, x, ex, sh, off)
+    assert np.all(gi[:, 0] == 9)
+    logits = oracle.router(x, r, "bf16")
+    assert np.array_equal(gs[:, 0], oracle.sigmoid(logits[:, 9]))
