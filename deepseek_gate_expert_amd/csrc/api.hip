@@ -37,8 +37,29 @@ size_t dispatch_ws_bytes(int64_t T, int32_t K, int32_t E) {
     return up((size_t)dispatch_blocks(T * K) * (size_t)E * sizeof(int32_t));
 }
 
+// Groups with more rows than this go to the LDS-tiled GEMMs (when T exceeds it); the rest are
+// streamed (each weight read once per 64 rows).
+constexpr int32_t STREAM_MAX_ROWS = 64;
+
+struct TilePlan {
+    bool on;
+    int32_t BM;
+    int32_t max_tiles;
+};
+
+// Shapes-only decision (no device reads): tiles of 256 rows when the average group is large.
+TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
+    TilePlan p{false, 128, 0};
+    if (d->act_dtype != MOE_BF16 || d->T <= STREAM_MAX_ROWS) return p;
+    p.on = true;
+    const int64_t avg = d->T * d->route.top_k / d->E;
+    p.BM = (allow256 && avg >= 192) ? 256 : 128;
+    p.max_tiles = tiled_max_tiles(d->T, d->route.top_k, d->E, p.BM);
+    return p;
+}
+
 struct FwdLayout {
-    size_t logits, inds, scores, blk, counts, offsets, sorted_slot, slot_row, h, o, total;
+    size_t logits, inds, scores, blk, counts, offsets, sorted_slot, slot_row, tiles, h, o, total;
 };
 
 FwdLayout fwd_layout(const moe_layer_desc* d) {
@@ -65,6 +86,8 @@ FwdLayout fwd_layout(const moe_layer_desc* d) {
     off += up(TK * 4);
     L.slot_row = off;
     off += up(TK * 4);
+    L.tiles = off;  // tile count + (group, row) pairs; sized for the smaller tile height
+    off += up(256 + 8 * (size_t)tiled_max_tiles(d->T, d->route.top_k, d->E, 128));
     L.h = off;
     off += up(rows * ldh * el);
     L.o = off;
@@ -87,6 +110,26 @@ int check_desc(const moe_layer_desc* d) {
 }
 
 inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Per device: 0 unknown, 1 tiles of 256 rows fit in LDS, 2 only 128, 3 tiled kernels unusable.
+int g_tiled_state[64];
+
+int tiled_state() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 3;
+    if (g_tiled_state[dev] == 0) {
+        int lds = 0;
+        hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        int st = 3;
+        if (configure_tiled_kernels() == hipSuccess) {
+            if (lds >= tiled_lds_bytes(256)) st = 1;
+            else if (lds >= tiled_lds_bytes(128)) st = 2;
+        }
+        (void)hipGetLastError();
+        g_tiled_state[dev] = st;
+    }
+    return g_tiled_state[dev];
+}
 
 // measurement hook state (see moe_set_stage_events)
 struct StageHook {
@@ -214,6 +257,8 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     int32_t* offsets = (int32_t*)(ws + L.offsets);
     int32_t* sorted_slot = (int32_t*)(ws + L.sorted_slot);
     int32_t* slot_row = (int32_t*)(ws + L.slot_row);
+    int32_t* tile_count = (int32_t*)(ws + L.tiles);
+    int32_t* tile_info = tile_count + 64;  // keep the pairs 256-byte aligned
 
     if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 0, s)))) return rc;
     if ((rc = hip_rc(launch_router(x, router_w, d->act_dtype, d->T, d->H, d->E, logit_offset, logits, s))))
@@ -264,26 +309,36 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     const int32_t E = d->E;
     const int32_t gend = E + (d->I_shared > 0 ? 1 : 0);
     const bool f32 = d->act_dtype == MOE_F32, q4 = d->expert_dtype == MOE_Q4G64;
+    TilePlan tp{false, 128, 0};
+    if (!f32) {
+        const int ts = tiled_state();
+        if (ts != 3) tp = plan_tiles(d, ts == 1);
+    }
+    a.stream_max_rows = tp.on ? STREAM_MAX_ROWS : 0x7fffffff;
+    // one expert-GEMM pass: weight-streaming kernels for small groups, tiled kernels for large
+    auto gemm = [&](bool first) -> int {
+        if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));
+        const int32_t rdt = q4 ? MOE_Q4G64 : MOE_BF16;
+        const int32_t split = q4 ? E : gend;  // 4-bit routed groups vs bf16 (shared) group
+        int r = hip_rc(first ? launch_gemm1_bf16(a, 0, split, rdt, s) : launch_gemm2_bf16(a, 0, split, rdt, s));
+        if (!r && tp.on)
+            r = hip_rc(launch_gemm_tiled(a, first, tp.BM, 0, split, rdt, tile_count, tile_info, tp.max_tiles, s));
+        if (!r && split < gend) {
+            r = hip_rc(first ? launch_gemm1_bf16(a, split, gend, MOE_BF16, s)
+                             : launch_gemm2_bf16(a, split, gend, MOE_BF16, s));
+            if (!r && tp.on)
+                r = hip_rc(launch_gemm_tiled(a, first, tp.BM, split, gend, MOE_BF16, tile_count, tile_info,
+                                             tp.max_tiles, s));
+        }
+        return r;
+    };
+    if (tp.on && (rc = hip_rc(launch_tiles(a, tp.BM, STREAM_MAX_ROWS, tile_count, tile_info, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_GEMM1, 0, s)))) return rc;
-    if (f32) {
-        rc = hip_rc(launch_gemm1_f32(a, s));
-    } else if (!q4) {
-        rc = hip_rc(launch_gemm1_bf16(a, 0, gend, MOE_BF16, s));
-    } else {
-        rc = hip_rc(launch_gemm1_bf16(a, 0, E, MOE_Q4G64, s));
-        if (!rc) rc = hip_rc(launch_gemm1_bf16(a, E, gend, MOE_BF16, s));
-    }
-    if (rc || (rc = hip_rc(mark(MOE_STAGE_GEMM1, 1, s)))) return rc;
+    if ((rc = gemm(true))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_GEMM1, 1, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_GEMM2, 0, s)))) return rc;
-    if (f32) {
-        rc = hip_rc(launch_gemm2_f32(a, s));
-    } else if (!q4) {
-        rc = hip_rc(launch_gemm2_bf16(a, 0, gend, MOE_BF16, s));
-    } else {
-        rc = hip_rc(launch_gemm2_bf16(a, 0, E, MOE_Q4G64, s));
-        if (!rc) rc = hip_rc(launch_gemm2_bf16(a, E, gend, MOE_BF16, s));
-    }
-    if (rc || (rc = hip_rc(mark(MOE_STAGE_GEMM2, 1, s)))) return rc;
+    if ((rc = gemm(false))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_GEMM2, 1, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 0, s)))) return rc;
     if ((rc = hip_rc(launch_combine(a, d->act_dtype, scores, slot_row, y, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 1, s)))) return rc;

@@ -48,6 +48,7 @@ struct GroupedArgs {
     const void* swg;             // shared [Is, H] act
     const void* swu;
     const void* swd;             // shared [H, Is] act
+    int32_t stream_max_rows;     // weight-streaming kernels skip groups with more rows than this
 };
 
 // launchers (return hipSuccess or the launch error)
@@ -65,6 +66,14 @@ hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32
 // fp32 layers: all routed rows and the shared rows in one launch each
 hipError_t launch_gemm1_f32(const GroupedArgs& a, hipStream_t s);
 hipError_t launch_gemm2_f32(const GroupedArgs& a, hipStream_t s);
+// tiled grouped GEMMs (groups with more than min_rows rows; tile list built on the device)
+int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM);
+int32_t tiled_lds_bytes(int32_t BM);
+hipError_t configure_tiled_kernels();
+hipError_t launch_tiles(const GroupedArgs& a, int32_t BM, int32_t min_rows, int32_t* tile_count, int32_t* tile_info,
+                        hipStream_t s);
+hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32_t g0, int32_t g1, int32_t wdt,
+                             const int32_t* tile_count, const int32_t* tile_info, int32_t max_tiles, hipStream_t s);
 hipError_t launch_combine(const GroupedArgs& a, int32_t act, const float* scores, const int32_t* slot_row,
                           void* y, hipStream_t s);
 

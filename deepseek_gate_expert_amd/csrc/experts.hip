@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void gemm1_stream(GroupedArgs a, int32_t g0) {
     const int32_t g = g0 + blockIdx.y;
     int32_t r0, cnt;
     group_rows(a, g, r0, cnt);
-    if (cnt <= 0) return;
+    if (cnt <= 0 || cnt > a.stream_max_rows) return;
     const bool shared = g == a.E;
     const int32_t N = shared ? a.Is : a.I;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void gemm2_stream(GroupedArgs a, int32_t g0) {
     const int32_t g = g0 + blockIdx.y;
     int32_t r0, cnt;
     group_rows(a, g, r0, cnt);
-    if (cnt <= 0) return;
+    if (cnt <= 0 || cnt > a.stream_max_rows) return;
     const bool shared = g == a.E;
     const int32_t KD = shared ? a.Is : a.I;  // reduction length
     const int32_t H = a.H;

@@ -96,6 +96,13 @@ EDGE = [
     ("f32_groups", synth.WORKLOADS["c0"].with_(T=30, E=16, K=4, G=4, TG=2, H=72)),
     ("zipf_skew", C1.with_(T=400, zipf_s=3.0, planted=0)),
     ("dsv3_decode_small_batch", synth.WORKLOADS["c2"].with_(T=3, H=512, I=256, Is=256)),
+    # T above the streaming limit: groups with more than 64 rows go to the LDS-tiled GEMMs
+    ("tiled_ragged_cols", C1.with_(T=300, H=320, I=192, Is=320, planted=0)),
+    ("tiled_q4", C1.with_(T=400, H=512, I=256, Is=192, expert="q4", planted=0)),
+    ("tiled_rows256", C1.with_(T=2048, H=256, I=128, Is=128, planted=0)),
+    ("tiled_rows256_q4", C1.with_(T=2048, H=256, I=128, Is=128, expert="q4", planted=0)),
+    ("tiled_1024_experts_shared", C1.with_(T=100, H=128, I=64, Is=64, E=1024, K=2, G=1, TG=1, planted=0)),
+    ("tiled_skewed", C1.with_(T=1500, H=192, I=128, Is=64, zipf_s=2.0, planted=0)),
 ]
 
 
