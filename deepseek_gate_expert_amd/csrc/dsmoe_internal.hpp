@@ -12,6 +12,7 @@ typedef uint16_t bf16_t;  // raw bf16 bits in memory
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native 16-byte vector (promotes to VGPRs)
 
 static_assert(sizeof(bf16x8) == 16, "bf16x8 is 16 bytes");
 

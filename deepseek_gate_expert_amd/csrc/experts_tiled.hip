@@ -35,24 +35,24 @@ constexpr int BK = 64;        // k per LDS stage (one 4-bit scale group)
 constexpr int NB = 256;       // weight rows per tile
 constexpr int THREADS = 256;  // 4 waves, 2 x 2
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // byte offset of 16-byte chunk c of row r in a [rows][64] bf16 LDS tile
 __device__ __forceinline__ uint32_t lds_off(int r, int c) { return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4)); }
 
-__device__ __forceinline__ uint4 dequant8(uint32_t w, float s, float b) {
-    uint4 r;
-    uint32_t* rp = (uint32_t*)&r;
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float b) {
+    u32x4 r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float lo = __builtin_fmaf(s, (float)((w >> (8 * j)) & 0xFu), b);
         const float hi = __builtin_fmaf(s, (float)((w >> (8 * j + 4)) & 0xFu), b);
-        rp[j] = pack_bf16x2(lo, hi);
+        r[j] = pack_bf16x2(lo, hi);
     }
     return r;
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// silu with the hardware reciprocal (about 1 ulp; the product is rounded to bf16 anyway)
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 struct TileArgs {
     GroupedArgs a;
@@ -62,6 +62,29 @@ struct TileArgs {
     int32_t col_tiles;          // output column tiles per row tile
     int32_t nwg;                // workgroups launched
 };
+
+// Workgroup -> (tile, column tile).  The logical space holds tile_count * col_tiles items in
+// bands of 4 column tiles: items of one band walk the row tiles with the column fastest, so the
+// workgroups running at once share both A panels (same rows) and B panels (same group and
+// columns).  Workgroup ids congruent mod 8 land on the same XCD; each XCD takes one contiguous
+// eighth of the logical space, sized by the tile count actually built (the grid is a bound).
+__device__ __forceinline__ bool map_tile(const TileArgs& ta, int32_t& tile, int32_t& ct) {
+    const int32_t ntiles = ta.tile_count[0];
+    const int32_t total = ntiles * ta.col_tiles;
+    const int32_t per_xcd = (total + 7) / 8;
+    const int32_t bid = blockIdx.x;
+    const int32_t pos = bid >> 3;
+    if (pos >= per_xcd) return false;
+    const int32_t l = (bid & 7) * per_xcd + pos;
+    if (l >= total) return false;
+    constexpr int32_t CB = 4;
+    const int32_t band = l / (ntiles * CB);
+    const int32_t bw = min(CB, ta.col_tiles - band * CB);
+    const int32_t rem = l - band * ntiles * CB;
+    tile = rem / bw;
+    ct = band * CB + rem % bw;
+    return true;
+}
 
 // SWIGLU = true: GEMM-1 (gate/up + SwiGLU -> h); false: GEMM-2 (down -> o)
 template <int BM, bool SWIGLU, int WF>
@@ -76,13 +99,8 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
     auto Bs = [&](int buf) -> char* { return smem + 2 * BM * 128 + buf * (NB * 128); };
 
     const GroupedArgs& a = ta.a;
-    // XCD-aware remap: ids i, i+8, i+16, ... run on one XCD; give them consecutive tiles.
-    const int32_t nwg8 = gridDim.x / 8;
-    const int32_t bid = blockIdx.x;
-    const int32_t logical = (bid & 7) * nwg8 + (bid >> 3);
-    if (logical >= ta.nwg) return;
-    const int32_t tile = logical / ta.col_tiles, ct = logical % ta.col_tiles;
-    if (tile >= ta.tile_count[0]) return;
+    int32_t tile, ct;
+    if (!map_tile(ta, tile, ct)) return;
     const int32_t g = ta.tile_info[2 * tile], m0 = ta.tile_info[2 * tile + 1];
     if (g < ta.g0 || g >= ta.g1) return;
     const bool shared = g == a.E;
@@ -103,8 +121,9 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- per-thread global sources ------------------------------------------------------
-    const bf16_t* a_src[A_LD];
+    // ---- per-thread global sources: uniform 64-bit bases + 32-bit element offsets -----------
+    const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
+    uint32_t a_off[A_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
         const int id = tid + THREADS * i;
@@ -114,112 +133,61 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
         const int c = id % 8;
         if (SWIGLU) {
             const int32_t tok = row < a.TK ? a.sorted_slot[row] / a.K : row - a.TK;
-            a_src[i] = (const bf16_t*)a.x + (int64_t)tok * a.H + c * 8;
+            a_off[i] = (uint32_t)tok * (uint32_t)a.H + c * 8;
         } else {
-            a_src[i] = (const bf16_t*)a.h + (int64_t)row * a.ldh + c * 8;
+            a_off[i] = (uint32_t)row * (uint32_t)a.ldh + c * 8;
         }
     }
-    // weight row (output column) of B-tile row `br`; columns past N are clamped (never stored)
-    auto w_row = [&](int br) -> int64_t {
-        const int32_t n = n0 + (SWIGLU ? br % (NB / 2) : br);
-        return n < N ? n : N - 1;
-    };
-    const bf16_t* b_src[B_LD];
-    const uint32_t* q_src[B_LD];
-    const bf16_t* s_src[B_LD];
-    const bf16_t* z_src[B_LD];
-    if constexpr (WF == WF_BF16) {
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int id = tid + THREADS * i;
-            const int br = id / 8, c = id % 8;
-            const int64_t n = w_row(br);
-            const bf16_t* base;
+    // weight matrices of this group (uniform); B-tile row br maps to output column w_row(br),
+    // clamped to N - 1 past the last column (such columns are never stored)
+    const bf16_t *wb0 = nullptr, *wb1 = nullptr;   // bf16: gate/up (GEMM-1) or down (both = down)
+    const uint32_t *qb0 = nullptr, *qb1 = nullptr; // 4-bit codes
+    const bf16_t *sb0 = nullptr, *sb1 = nullptr, *zb0 = nullptr, *zb1 = nullptr;
+    {
+        const int32_t out_dim = SWIGLU ? a.I : a.H;
+        const int64_t eoff = (int64_t)g * out_dim;  // first row of this expert
+        if (WF == WF_BF16) {
             if (SWIGLU) {
-                const bool up = br >= NB / 2;
-                base = shared ? (const bf16_t*)(up ? a.swu : a.swg)
-                              : (const bf16_t*)(up ? a.wu : a.wg) + (int64_t)g * a.I * a.H;
+                wb0 = shared ? (const bf16_t*)a.swg : (const bf16_t*)a.wg + eoff * KD;
+                wb1 = shared ? (const bf16_t*)a.swu : (const bf16_t*)a.wu + eoff * KD;
             } else {
-                base = shared ? (const bf16_t*)a.swd : (const bf16_t*)a.wd + (int64_t)g * a.H * a.I;
+                wb0 = wb1 = shared ? (const bf16_t*)a.swd : (const bf16_t*)a.wd + eoff * KD;
             }
-            b_src[i] = base + n * KD + c * 8;
-            q_src[i] = nullptr;
-            s_src[i] = z_src[i] = nullptr;
-        }
-    } else {
-        // 4-bit: one 16-byte load covers 32 k of one row; a row of a 64-k step is two loads
-#pragma unroll
-        for (int i = 0; i < B_LD / 4; ++i) {
-            const int id = tid + THREADS * i;  // NB * 2 = 512 half-rows per step
-            const int br = id / 2, hf = id % 2;
-            const int64_t n = w_row(br);
-            int32_t out_dim;
-            const uint32_t* qb;
-            const bf16_t *sb, *zb;
+        } else {
             if (SWIGLU) {
-                const bool up = br >= NB / 2;
-                out_dim = a.I;
-                qb = (const uint32_t*)(up ? a.wu : a.wg);
-                sb = up ? a.su : a.sg;
-                zb = up ? a.bu : a.bg;
+                qb0 = (const uint32_t*)a.wg + eoff * (KD / 8);
+                qb1 = (const uint32_t*)a.wu + eoff * (KD / 8);
+                sb0 = a.sg + eoff * (KD / 64);
+                sb1 = a.su + eoff * (KD / 64);
+                zb0 = a.bg + eoff * (KD / 64);
+                zb1 = a.bu + eoff * (KD / 64);
             } else {
-                out_dim = a.H;
-                qb = (const uint32_t*)a.wd;
-                sb = a.sd;
-                zb = a.bd;
+                qb0 = qb1 = (const uint32_t*)a.wd + eoff * (KD / 8);
+                sb0 = sb1 = a.sd + eoff * (KD / 64);
+                zb0 = zb1 = a.bd + eoff * (KD / 64);
             }
-            const int64_t row = (int64_t)g * out_dim + n;
-            q_src[i] = qb + row * (KD / 8) + hf * 4;
-            s_src[i] = sb + row * (KD / 64);
-            z_src[i] = zb + row * (KD / 64);
-            b_src[i] = nullptr;
         }
     }
+    constexpr int QL = B_LD / 4;  // 4-bit: 16-byte code loads per thread per step
+    uint32_t b_off[WF == WF_BF16 ? B_LD : QL];
+    bool b_hi[WF == WF_BF16 ? B_LD : QL];  // row belongs to the second matrix (up)
+#pragma unroll
+    for (int i = 0; i < (WF == WF_BF16 ? B_LD : QL); ++i) {
+        const int id = tid + THREADS * i;
+        const int br = WF == WF_BF16 ? id / 8 : id / 2;
+        int32_t n = n0 + (SWIGLU ? br % (NB / 2) : br);
+        n = n < N ? n : N - 1;
+        b_hi[i] = SWIGLU && br >= NB / 2;
+        if (WF == WF_BF16)
+            b_off[i] = (uint32_t)n * (uint32_t)KD + (id % 8) * 8;
+        else
+            b_off[i] = (uint32_t)n * (uint32_t)(KD / 8) + (id % 2) * 4;  // word offset of the half row
+    }
 
-    // ---- staging registers ------------------------------------------------------------
-    uint4 ra[A_LD];
-    uint4 rb[WF == WF_BF16 ? B_LD : B_LD / 4];
-    float rs[WF == WF_BF16 ? 1 : B_LD / 4], rz[WF == WF_BF16 ? 1 : B_LD / 4];
-
-    auto gload = [&](int32_t k) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i) ra[i] = *(const uint4*)(a_src[i] + k);
-        if constexpr (WF == WF_BF16) {
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i) rb[i] = *(const uint4*)(b_src[i] + k);
-        } else {
-#pragma unroll
-            for (int i = 0; i < B_LD / 4; ++i) {
-                rb[i] = *(const uint4*)(q_src[i] + k / 8);
-                rs[i] = bf16_to_f32(s_src[i][k / 64]);
-                rz[i] = bf16_to_f32(z_src[i][k / 64]);
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int id = tid + THREADS * i;
-            *(uint4*)(As(buf) + lds_off(id / 8, id % 8)) = ra[i];
-        }
-        if constexpr (WF == WF_BF16) {
-#pragma unroll
-            for (int i = 0; i < B_LD; ++i) {
-                const int id = tid + THREADS * i;
-                *(uint4*)(Bs(buf) + lds_off(id / 8, id % 8)) = rb[i];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < B_LD / 4; ++i) {
-                const int id = tid + THREADS * i;
-                const int br = id / 2, hf = id % 2;
-                const uint32_t* w = (const uint32_t*)&rb[i];
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *(uint4*)(Bs(buf) + lds_off(br, hf * 4 + j)) = dequant8(w[j], rs[i], rz[i]);
-            }
-        }
-    };
+    // ---- staging registers --------------------------------------------------------------
+    u32x4 ra[A_LD];
+    u32x4 rb[WF == WF_BF16 ? B_LD : QL];
+    float rs[QL], rz[QL];
 
     // ---- accumulators -------------------------------------------------------------------
     // wave tile: WM rows x 128 weight rows = MT x 4 MFMA tiles of 32 x 32
@@ -240,12 +208,55 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
     }
 
     const int nk = KD / BK;
-    gload(0);
-    lstore(0);
+#define DSMOE_GLOAD(K0)                                                                       \
+    do {                                                                                      \
+        const int32_t k_ = (K0);                                                              \
+        _Pragma("unroll") for (int i = 0; i < A_LD; ++i) ra[i] = *(const u32x4*)(a_base + a_off[i] + k_); \
+        if constexpr (WF == WF_BF16) {                                                        \
+            _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                                  \
+                rb[i] = *(const u32x4*)((b_hi[i] ? wb1 : wb0) + b_off[i] + k_);               \
+        } else {                                                                              \
+            _Pragma("unroll") for (int i = 0; i < QL; ++i) {                                  \
+                const int br_ = (tid + THREADS * i) / 2;                                      \
+                int32_t n_ = n0 + (SWIGLU ? br_ % (NB / 2) : br_);                            \
+                n_ = n_ < N ? n_ : N - 1;                                                     \
+                const uint32_t so_ = (uint32_t)n_ * (uint32_t)(KD / 64) + k_ / 64;            \
+                rb[i] = *(const u32x4*)((b_hi[i] ? qb1 : qb0) + b_off[i] + k_ / 8);           \
+                rs[i] = bf16_to_f32((b_hi[i] ? sb1 : sb0)[so_]);                              \
+                rz[i] = bf16_to_f32((b_hi[i] ? zb1 : zb0)[so_]);                              \
+            }                                                                                 \
+        }                                                                                     \
+    } while (0)
+#define DSMOE_LSTORE(BUF)                                                                     \
+    do {                                                                                      \
+        char* as_ = As(BUF);                                                                  \
+        char* bs_ = Bs(BUF);                                                                  \
+        _Pragma("unroll") for (int i = 0; i < A_LD; ++i) {                                    \
+            const int id = tid + THREADS * i;                                                 \
+            *(u32x4*)(as_ + lds_off(id / 8, id % 8)) = ra[i];                                 \
+        }                                                                                     \
+        if constexpr (WF == WF_BF16) {                                                        \
+            _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                                \
+                const int id = tid + THREADS * i;                                             \
+                *(u32x4*)(bs_ + lds_off(id / 8, id % 8)) = rb[i];                             \
+            }                                                                                 \
+        } else {                                                                              \
+            _Pragma("unroll") for (int i = 0; i < QL; ++i) {                                  \
+                const int id = tid + THREADS * i;                                             \
+                const int br_ = id / 2, hf_ = id % 2;                                         \
+                *(u32x4*)(bs_ + lds_off(br_, hf_ * 4 + 0)) = dequant8(rb[i][0], rs[i], rz[i]); \
+                *(u32x4*)(bs_ + lds_off(br_, hf_ * 4 + 1)) = dequant8(rb[i][1], rs[i], rz[i]); \
+                *(u32x4*)(bs_ + lds_off(br_, hf_ * 4 + 2)) = dequant8(rb[i][2], rs[i], rz[i]); \
+                *(u32x4*)(bs_ + lds_off(br_, hf_ * 4 + 3)) = dequant8(rb[i][3], rs[i], rz[i]); \
+            }                                                                                 \
+        }                                                                                     \
+    } while (0)
+    DSMOE_GLOAD(0);
+    DSMOE_LSTORE(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+        if (kt + 1 < nk) DSMOE_GLOAD((kt + 1) * BK);
         const char* Ab = As(buf);
         const char* Bb = Bs(buf);
 #pragma unroll
@@ -255,12 +266,12 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 const int r = wm * WM + i * 32 + (lane & 31);
-                af[i] = as_bf16x8(*(const uint4*)(Ab + lds_off(r, c)));
+                af[i] = as_bf16x8(*(const u32x4*)(Ab + lds_off(r, c)));
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = brow[j] + (lane & 31);
-                bfr[j] = as_bf16x8(*(const uint4*)(Bb + lds_off(r, c)));
+                bfr[j] = as_bf16x8(*(const u32x4*)(Bb + lds_off(r, c)));
             }
 #pragma unroll
             for (int i = 0; i < MT; ++i)
@@ -268,11 +279,203 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
+        if (kt + 1 < nk) DSMOE_LSTORE(buf ^ 1);
         __syncthreads();
     }
+#undef DSMOE_GLOAD
+#undef DSMOE_LSTORE
 
     // ---- epilogue -----------------------------------------------------------------------
+    const int col_l = lane & 31, rgrp = (lane >> 5) * 4;
+    if (SWIGLU) {
+        bf16_t* h = (bf16_t*)a.h;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int32_t col = n0 + wn * 64 + j * 32 + col_l;
+                if (col >= N) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int32_t rr = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
+                    if (rr < cnt)
+                        h[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 2][v]);
+                }
+            }
+    } else {
+        bf16_t* o = (bf16_t*)a.o;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int32_t col = n0 + wn * 128 + j * 32 + col_l;
+                if (col >= N) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int32_t rr = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
+                    if (rr < cnt) o[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[i][j][v]);
+                }
+            }
+    }
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// bf16 weights: direct-to-LDS loads into a 4-stage ring.
+//
+// global_load_lds_dwordx4 moves 16 bytes per lane straight into LDS (lane i of an instruction
+// fills bytes [16 i, 16 i + 16) of a 1 KB block), so no staging registers are needed and three
+// k-stages of 32 can be in flight while the matrix cores work on the fourth.  LDS rows are 64
+// bytes (32 bf16); the four 16-byte chunks of row r sit at chunk c ^ ((r >> 1) & 3), which makes
+// the eight lanes of each ds_read_b128 phase hit eight distinct 16-byte bank groups.  A lane of a
+// DMA instruction therefore fetches the logical chunk that its LDS slot holds.  The compiler
+// does not track these LDS writes, so the waits are explicit: before stage s is read, each wave
+// waits until at most the later stages' loads are outstanding (vmcnt) and then meets the others
+// at a barrier; the slot refilled after that barrier is the one every wave finished reading in
+// the previous iteration.
+// ---------------------------------------------------------------------------------------------
+namespace dma {
+constexpr int BKD = 32;        // k per stage
+constexpr int ROWB = 64;       // bytes per LDS row
+constexpr int NST = 4;         // ring depth
+__device__ __forceinline__ uint32_t off(int r, int c) { return (uint32_t)(r * ROWB + ((c ^ ((r >> 1) & 3)) << 4)); }
+}  // namespace dma
+
+#define DSMOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int BM, bool SWIGLU>
+__global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
+    using namespace dma;
+    constexpr int WM = BM / 2;
+    constexpr int MT = WM / 32;
+    constexpr int A_BYTES = BM * ROWB, B_BYTES = NB * ROWB, ST_BYTES = A_BYTES + B_BYTES;
+    constexpr int A_DMA = A_BYTES / 1024 / 4;  // DMA instructions per wave per stage
+    constexpr int B_DMA = B_BYTES / 1024 / 4;
+    constexpr int D = A_DMA + B_DMA;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const GroupedArgs& a = ta.a;
+    int32_t tile, ct;
+    if (!map_tile(ta, tile, ct)) return;
+    const int32_t g = ta.tile_info[2 * tile], m0 = ta.tile_info[2 * tile + 1];
+    if (g < ta.g0 || g >= ta.g1) return;
+    const bool shared = g == a.E;
+    int32_t r0, cnt;
+    if (!shared) {
+        r0 = a.offsets[g];
+        cnt = a.offsets[g + 1] - r0;
+    } else {
+        r0 = a.TK;
+        cnt = (int32_t)a.T;
+    }
+    const int32_t N = SWIGLU ? (shared ? a.Is : a.I) : a.H;
+    const int32_t KD = SWIGLU ? a.H : (shared ? a.Is : a.I);
+    constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
+    const int32_t n0 = ct * OUT_COLS;
+    if (n0 >= N) return;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // ---- DMA sources: instruction j of this wave fills LDS rows [16 (wave*X + j), +16) -----
+    const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
+    uint32_t a_off[A_DMA];
+#pragma unroll
+    for (int j = 0; j < A_DMA; ++j) {
+        const int r = (wave * A_DMA + j) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 1) & 3);
+        int32_t rr = m0 + r;
+        rr = rr < cnt ? rr : cnt - 1;  // rows past the group are computed, never stored
+        const int32_t row = r0 + rr;
+        if (SWIGLU) {
+            const int32_t tok = row < a.TK ? a.sorted_slot[row] / a.K : row - a.TK;
+            a_off[j] = (uint32_t)tok * (uint32_t)a.H + c * 8;
+        } else {
+            a_off[j] = (uint32_t)row * (uint32_t)a.ldh + c * 8;
+        }
+    }
+    const bf16_t *wb0, *wb1;
+    {
+        const int64_t eoff = (int64_t)g * (SWIGLU ? a.I : a.H);
+        if (SWIGLU) {
+            wb0 = shared ? (const bf16_t*)a.swg : (const bf16_t*)a.wg + eoff * KD;
+            wb1 = shared ? (const bf16_t*)a.swu : (const bf16_t*)a.wu + eoff * KD;
+        } else {
+            wb0 = wb1 = shared ? (const bf16_t*)a.swd : (const bf16_t*)a.wd + eoff * KD;
+        }
+    }
+    uint32_t b_off[B_DMA];
+#pragma unroll
+    for (int j = 0; j < B_DMA; ++j) {
+        const int br = (wave * B_DMA + j) * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((br >> 1) & 3);
+        int32_t n = n0 + (SWIGLU ? br % (NB / 2) : br);
+        n = n < N ? n : N - 1;  // columns past N are computed, never stored
+        b_off[j] = (uint32_t)n * (uint32_t)KD + c * 8;
+    }
+    // a wave's B instruction j covers 16 rows, all gate or all up (NB/2 is a multiple of 16)
+    auto issue = [&](int kt) {
+        char* st = smem + (kt & (NST - 1)) * ST_BYTES;
+        const int32_t k0 = kt * BKD;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(a_base + a_off[j] + k0),
+                                             DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j) {
+            const int br0 = (wave * B_DMA + j) * 16;
+            const bf16_t* wb = (SWIGLU && br0 >= NB / 2) ? wb1 : wb0;
+            __builtin_amdgcn_global_load_lds((const void*)(wb + b_off[j] + k0),
+                                             DSMOE_LDS_PTR(st + A_BYTES + (wave * B_DMA + j) * 1024), 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    int brow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) brow[j] = SWIGLU ? (j < 2 ? 0 : NB / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+
+    const int nk = KD / BKD;  // >= 2
+    issue(0);
+    issue(1);
+    if (nk > 2) issue(2);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int ahead = min(nk - 1 - kt, 2);
+        if (ahead == 2)
+            wait_vm_barrier<2 * D>();
+        else if (ahead == 1)
+            wait_vm_barrier<D>();
+        else
+            wait_vm_barrier<0>();
+        if (kt + 3 < nk) issue(kt + 3);
+        const char* st = smem + (kt & (NST - 1)) * ST_BYTES;
+#pragma unroll
+        for (int s = 0; s < BKD / 16; ++s) {
+            const int c = 2 * s + (lane >> 5);
+            bf16x8 af[MT], bfr[4];
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                af[i] = as_bf16x8(*(const u32x4*)(st + off(wm * WM + i * 32 + (lane & 31), c)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bfr[j] = as_bf16x8(*(const u32x4*)(st + A_BYTES + off(brow[j] + (lane & 31), c)));
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
     const int col_l = lane & 31, rgrp = (lane >> 5) * 4;
     if (SWIGLU) {
         bf16_t* h = (bf16_t*)a.h;
@@ -348,6 +551,14 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
     }
 }
 
+template <int BM, bool SW>
+hipError_t launch_dma_t(const TileArgs& ta, hipStream_t s) {
+    const size_t lds = (size_t)dma::NST * (BM + NB) * dma::ROWB;
+    const unsigned grid = (unsigned)(((ta.nwg + 7) / 8) * 8);
+    hipLaunchKernelGGL((gemm_dma<BM, SW>), dim3(grid), dim3(THREADS), lds, s, ta);
+    return hipGetLastError();
+}
+
 template <int BM, bool SW, int WF>
 hipError_t launch_tiled_t(const TileArgs& ta, hipStream_t s) {
     const size_t lds = 2 * (size_t)(BM + NB) * 128;
@@ -363,20 +574,23 @@ int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM) {
     return (int32_t)((rows + BM - 1) / BM + E + 1);
 }
 
-int32_t tiled_lds_bytes(int32_t BM) { return 2 * (BM + NB) * 128; }
+// largest dynamic LDS any tiled kernel of this tile height uses
+int32_t tiled_lds_bytes(int32_t BM) {
+    const int32_t reg_staged = 2 * (BM + NB) * 128, dma_ring = dma::NST * (BM + NB) * dma::ROWB;
+    return reg_staged > dma_ring ? reg_staged : dma_ring;
+}
 
 hipError_t configure_tiled_kernels() {
     // allow the large dynamic LDS allocations (up to 128 KB) of the tiled kernels
     const void* ks[] = {
-        (const void*)gemm_tiled<256, true, WF_BF16>, (const void*)gemm_tiled<256, false, WF_BF16>,
-        (const void*)gemm_tiled<256, true, WF_Q4>,   (const void*)gemm_tiled<256, false, WF_Q4>,
-        (const void*)gemm_tiled<128, true, WF_BF16>, (const void*)gemm_tiled<128, false, WF_BF16>,
-        (const void*)gemm_tiled<128, true, WF_Q4>,   (const void*)gemm_tiled<128, false, WF_Q4>,
+        (const void*)gemm_dma<256, true>,          (const void*)gemm_dma<256, false>,
+        (const void*)gemm_tiled<256, true, WF_Q4>, (const void*)gemm_tiled<256, false, WF_Q4>,
+        (const void*)gemm_dma<128, true>,          (const void*)gemm_dma<128, false>,
+        (const void*)gemm_tiled<128, true, WF_Q4>, (const void*)gemm_tiled<128, false, WF_Q4>,
     };
     const int bms[] = {256, 256, 256, 256, 128, 128, 128, 128};
     for (int i = 0; i < 8; ++i) {
-        const int lds = 2 * (bms[i] + NB) * 128;
-        hipError_t e = hipFuncSetAttribute(ks[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipError_t e = hipFuncSetAttribute(ks[i], hipFuncAttributeMaxDynamicSharedMemorySize, tiled_lds_bytes(bms[i]));
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -403,12 +617,12 @@ hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32
     ta.col_tiles = (N + out_cols - 1) / out_cols;
     ta.nwg = max_tiles * ta.col_tiles;
     const bool q4 = wdt == MOE_Q4G64;
-    if (BM == 256) {
-        if (gemm1) return q4 ? launch_tiled_t<256, true, WF_Q4>(ta, s) : launch_tiled_t<256, true, WF_BF16>(ta, s);
-        return q4 ? launch_tiled_t<256, false, WF_Q4>(ta, s) : launch_tiled_t<256, false, WF_BF16>(ta, s);
+    if (!q4) {
+        if (BM == 256) return gemm1 ? launch_dma_t<256, true>(ta, s) : launch_dma_t<256, false>(ta, s);
+        return gemm1 ? launch_dma_t<128, true>(ta, s) : launch_dma_t<128, false>(ta, s);
     }
-    if (gemm1) return q4 ? launch_tiled_t<128, true, WF_Q4>(ta, s) : launch_tiled_t<128, true, WF_BF16>(ta, s);
-    return q4 ? launch_tiled_t<128, false, WF_Q4>(ta, s) : launch_tiled_t<128, false, WF_BF16>(ta, s);
+    if (BM == 256) return gemm1 ? launch_tiled_t<256, true, WF_Q4>(ta, s) : launch_tiled_t<256, false, WF_Q4>(ta, s);
+    return gemm1 ? launch_tiled_t<128, true, WF_Q4>(ta, s) : launch_tiled_t<128, false, WF_Q4>(ta, s);
 }
 
 }  // namespace dsmoe
