@@ -458,22 +458,29 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
             wait_vm_barrier<0>();
         if (kt + 3 < nk) issue(kt + 3);
         const char* st = smem + (kt & (NST - 1)) * ST_BYTES;
+        // all operand fragments of the stage first, then the MFMAs: only the first MFMA waits
+        // for LDS, the remaining reads land while the matrix cores are busy
+        constexpr int KS = BKD / 16;
+        bf16x8 af[KS][MT], bfr[KS][4];
 #pragma unroll
-        for (int s = 0; s < BKD / 16; ++s) {
+        for (int s = 0; s < KS; ++s) {
             const int c = 2 * s + (lane >> 5);
-            bf16x8 af[MT], bfr[4];
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-                af[i] = as_bf16x8(*(const u32x4*)(st + off(wm * WM + i * 32 + (lane & 31), c)));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bfr[j] = as_bf16x8(*(const u32x4*)(st + A_BYTES + off(brow[j] + (lane & 31), c)));
+                bfr[s][j] = as_bf16x8(*(const u32x4*)(st + A_BYTES + off(brow[j] + (lane & 31), c)));
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+                af[s][i] = as_bf16x8(*(const u32x4*)(st + off(wm * WM + i * 32 + (lane & 31), c)));
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int i = 0; i < MT; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, KS * (MT + 4), 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, KS * MT * 4, 0);    // MFMAs
     }
 
     const int col_l = lane & 31, rgrp = (lane >> 5) * 4;

@@ -7,11 +7,9 @@
 // Every output element is accumulated by one fused multiply-add per k, k ascending, starting
 // from +0.0f, then one fp32 add of the offset.  Because the order is fixed the logits are
 // reproducible bit for bit, which keeps the expert selection stable.  That rules out MFMA
-// (its internal summation order is not specified), so this is a VALU kernel: a workgroup
-// stages a [BM tokens x 32] tile of x and a [BN experts x 32] tile of W in LDS as fp32
-// (k-major, so a thread reads its MT tokens / NT experts at one k as one vector), and each
-// thread keeps an MT x NT register tile of accumulators.  The k loop is never split across
-// threads.  The zero tail of a partial k chunk is never fed to an FMA.
+// (its internal summation order is not specified), so these are VALU kernels in which the k
+// loop of an output is never split across threads and the zero tail of a partial k chunk is
+// never fed to an FMA.
 #include "dsmoe_internal.hpp"
 
 namespace dsmoe {
@@ -26,16 +24,71 @@ __device__ __forceinline__ float ld_act<bf16_t>(const bf16_t* p, int64_t i) { re
 
 constexpr int KC = 32;
 
+// 8 consecutive activations as fp32 (16- or 32-byte vector loads)
+template <typename TA>
+__device__ __forceinline__ void ld8(const TA* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void ld8<bf16_t>(const bf16_t* p, float (&v)[8]) {
+    const u32x4 q = *(const u32x4*)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(q[i] << 16);
+        v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void ld8<float>(const float* p, float (&v)[8]) {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = a[i];
+        v[4 + i] = b[i];
+    }
+}
+
+// 8 activations starting at element i of row `row` (length H), zero past the end of the row
+template <typename TA>
+__device__ __forceinline__ void ld8_row(const TA* row, int32_t i, int32_t H, bool vec, float (&v)[8]) {
+    if (vec && i + 8 <= H) {
+        ld8<TA>(row + i, v);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (i + j < H) ? ld_act(row, i + j) : 0.0f;
+    }
+}
+
+// Many tokens: 256 threads, MT x NT register tile per thread (BM = 16 MT tokens x BN = 16 NT
+// experts per workgroup), k chunks of 32 staged in LDS as fp32 (k-major), double buffered: the
+// next chunk's global loads are in flight while the current chunk is multiplied.
 template <typename TA, int MT, int NT>
 __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, const TA* __restrict__ w,
                                                      const float* __restrict__ off, float* __restrict__ logits,
                                                      int64_t T, int32_t H, int32_t E) {
     constexpr int BM = 16 * MT, BN = 16 * NT;
-    __shared__ float xs[KC][BM + 4];
-    __shared__ float ws[KC][BN + 4];
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int32_t n0 = blockIdx.x * BN;
+    constexpr int XL = BM * KC / 8 / 256, WL = BN * KC / 8 / 256;  // 8-element loads per thread
+    static_assert(XL >= 1 && WL >= 1, "tile too small for the staging layout");
+    __shared__ float xs[2][KC][BM + 4];
+    __shared__ float ws[2][KC][BN + 4];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int64_t m0 = (int64_t)blockIdx.x * BM;
+    const int32_t n0 = blockIdx.y * BN;
+    const bool vec = (H % 8) == 0;
+
+    // staging assignment: load i of this thread covers row (tid + 256 i) / 4, k (tid % 4) * 8
+    const TA* xrow[XL];
+    const TA* wrow[WL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+        int64_t t = m0 + (tid + 256 * i) / 4;
+        xrow[i] = x + (t < T ? t : T - 1) * H;
+    }
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+        int32_t e = n0 + (tid + 256 * i) / 4;
+        wrow[i] = w + (int64_t)(e < E ? e : E - 1) * H;
+    }
+    const int kq = (tid & 3) * 8;
+    float xv[XL][8], wv[WL][8];
 
     float acc[MT][NT];
 #pragma unroll
@@ -43,31 +96,42 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = 0.0f;
 
-    for (int32_t k0 = 0; k0 < H; k0 += KC) {
-        const int kc = min(KC, H - k0);
-        for (int i = threadIdx.x; i < BM * KC; i += 256) {
-            const int m = i / KC, k = i % KC;
-            const int64_t t = m0 + m;
-            xs[k][m] = (t < T && k < kc) ? ld_act(x, t * H + k0 + k) : 0.0f;
-        }
-        for (int i = threadIdx.x; i < BN * KC; i += 256) {
-            const int n = i / KC, k = i % KC;
-            const int32_t e = n0 + n;
-            ws[k][n] = (e < E && k < kc) ? ld_act(w, (int64_t)e * H + k0 + k) : 0.0f;
-        }
+    const int nch = (H + KC - 1) / KC;
+#pragma unroll
+    for (int i = 0; i < XL; ++i) ld8_row(xrow[i], kq, H, vec, xv[i]);
+#pragma unroll
+    for (int i = 0; i < WL; ++i) ld8_row(wrow[i], kq, H, vec, wv[i]);
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+#pragma unroll
+        for (int i = 0; i < XL; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xs[b][kq + j][(tid + 256 * i) / 4] = xv[i][j];
+#pragma unroll
+        for (int i = 0; i < WL; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ws[b][kq + j][(tid + 256 * i) / 4] = wv[i][j];
         __syncthreads();
+        if (c + 1 < nch) {
+            const int32_t kn = (c + 1) * KC + kq;
+#pragma unroll
+            for (int i = 0; i < XL; ++i) ld8_row(xrow[i], kn, H, vec, xv[i]);
+#pragma unroll
+            for (int i = 0; i < WL; ++i) ld8_row(wrow[i], kn, H, vec, wv[i]);
+        }
+        const int kc = min(KC, H - c * KC);  // the zero tail of the last chunk is never used
         for (int k = 0; k < kc; ++k) {
-            float a[MT], b[NT];
+            float a[MT], bb[NT];
 #pragma unroll
-            for (int i = 0; i < MT; ++i) a[i] = xs[k][ty * MT + i];
+            for (int i = 0; i < MT; ++i) a[i] = xs[b][k][ty * MT + i];
 #pragma unroll
-            for (int j = 0; j < NT; ++j) b[j] = ws[k][tx * NT + j];
+            for (int j = 0; j < NT; ++j) bb[j] = ws[b][k][tx * NT + j];
 #pragma unroll
             for (int i = 0; i < MT; ++i)
 #pragma unroll
-                for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
         }
-        __syncthreads();
+        // buffer b is rewritten two chunks later, after the next iteration's barrier
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -84,10 +148,89 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
     }
 }
 
+// Few tokens: a workgroup is ONE wave that computes one expert for 64 tokens (lane = token),
+// so even a single 64-token batch spreads over E workgroups.  Each lane streams its own token's
+// row of x and the (wave-uniform) expert row in chunks of 32 k, kept in a ring of four register
+// buffers so that three chunks of loads are in flight while the current one is multiplied.
+// One accumulator per lane, k ascending.  grid: x = E, y = ceil(T / 64).
+constexpr int GV_CK = 32;
+
+template <typename TA>
+__device__ __forceinline__ void fma_chunk(const u32x4 (&xq)[GV_CK * sizeof(TA) / 16],
+                                          const u32x4 (&wq)[GV_CK * sizeof(TA) / 16], float& acc);
+template <>
+__device__ __forceinline__ void fma_chunk<bf16_t>(const u32x4 (&xq)[4], const u32x4 (&wq)[4], float& acc) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = __builtin_fmaf(__uint_as_float(xq[v][i] << 16), __uint_as_float(wq[v][i] << 16), acc);
+            acc = __builtin_fmaf(__uint_as_float(xq[v][i] & 0xffff0000u), __uint_as_float(wq[v][i] & 0xffff0000u),
+                                 acc);
+        }
+}
+template <>
+__device__ __forceinline__ void fma_chunk<float>(const u32x4 (&xq)[8], const u32x4 (&wq)[8], float& acc) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(__uint_as_float(xq[v][i]), __uint_as_float(wq[v][i]), acc);
+}
+
+template <typename TA>
+__global__ __launch_bounds__(64) void router_gemv(const TA* __restrict__ x, const TA* __restrict__ w,
+                                                  const float* __restrict__ off, float* __restrict__ logits,
+                                                  int64_t T, int32_t H, int32_t E) {
+    constexpr int NV = GV_CK * (int)sizeof(TA) / 16;  // 16-byte vectors per chunk
+    const int lane = threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.y * 64 + lane;
+    const int32_t e = blockIdx.x;
+    const TA* xr = x + (t < T ? t : T - 1) * H;
+    const TA* wr = w + (int64_t)e * H;
+    float acc = 0.0f;
+    const int nch = H / GV_CK;
+    if (H % GV_CK == 0) {
+        u32x4 xb[4][NV], wb[4][NV];
+#define DSMOE_GV_LOAD(SLOT, C)                                                       \
+    do {                                                                             \
+        _Pragma("unroll") for (int v_ = 0; v_ < NV; ++v_) {                          \
+            xb[SLOT][v_] = *(const u32x4*)(xr + (C) * GV_CK + v_ * (16 / sizeof(TA))); \
+            wb[SLOT][v_] = *(const u32x4*)(wr + (C) * GV_CK + v_ * (16 / sizeof(TA))); \
+        }                                                                            \
+    } while (0)
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+            if (u < nch) DSMOE_GV_LOAD(u, u);
+        for (int c = 0; c < nch; c += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (c + u + 3 < nch) DSMOE_GV_LOAD((u + 3) & 3, c + u + 3);
+                if (c + u < nch) fma_chunk<TA>(xb[u], wb[u], acc);
+            }
+        }
+#undef DSMOE_GV_LOAD
+    } else {
+        for (int32_t k = 0; k < H; ++k) acc = __builtin_fmaf(ld_act(xr, k), ld_act(wr, k), acc);
+    }
+    if (t < T) {
+        float v = acc;
+        if (off) v = v + off[e];
+        logits[t * E + e] = v;
+    }
+}
+
+template <typename TA>
+hipError_t launch_gemv(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, const float* off, float* logits,
+                       hipStream_t s) {
+    const dim3 grid(E, (unsigned)((T + 63) / 64));
+    hipLaunchKernelGGL(router_gemv<TA>, grid, dim3(64), 0, s, x, w, off, logits, T, H, E);
+    return hipGetLastError();
+}
+
 template <typename TA, int MT, int NT>
 hipError_t launch_t(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, const float* off, float* logits,
                     hipStream_t s) {
-    const dim3 grid((E + 16 * NT - 1) / (16 * NT), (unsigned)((T + 16 * MT - 1) / (16 * MT)));
+    const dim3 grid((unsigned)((T + 16 * MT - 1) / (16 * MT)), (E + 16 * NT - 1) / (16 * NT));
     hipLaunchKernelGGL((router_kernel<TA, MT, NT>), grid, dim3(256), 0, s, x, w, off, logits, T, H, E);
     return hipGetLastError();
 }
@@ -97,17 +240,17 @@ hipError_t launch_t(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, c
 hipError_t launch_router(const void* x, const void* w, int32_t act, int64_t T, int32_t H, int32_t E,
                          const float* offset, float* logits, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    const bool big = T * (int64_t)E >= (int64_t)1 << 19;  // enough outputs for 4x4 register tiles
+    // few tokens: one output per lane (GEMV shape); many: 4 x 4 register tiles (64 x 64 per workgroup)
     if (act == MOE_BF16) {
         const bf16_t* xb = (const bf16_t*)x;
         const bf16_t* wb = (const bf16_t*)w;
-        return big ? launch_t<bf16_t, 4, 4>(xb, wb, T, H, E, offset, logits, s)
-                   : launch_t<bf16_t, 1, 1>(xb, wb, T, H, E, offset, logits, s);
+        if (T <= 512) return launch_gemv<bf16_t>(xb, wb, T, H, E, offset, logits, s);
+        return launch_t<bf16_t, 4, 4>(xb, wb, T, H, E, offset, logits, s);
     }
     const float* xf = (const float*)x;
     const float* wf = (const float*)w;
-    return big ? launch_t<float, 4, 4>(xf, wf, T, H, E, offset, logits, s)
-               : launch_t<float, 1, 1>(xf, wf, T, H, E, offset, logits, s);
+    if (T <= 512) return launch_gemv<float>(xf, wf, T, H, E, offset, logits, s);
+    return launch_t<float, 4, 4>(xf, wf, T, H, E, offset, logits, s);
 }
 
 }  // namespace dsmoe
