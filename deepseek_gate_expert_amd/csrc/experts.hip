@@ -8,13 +8,17 @@
 // for every row r of group g (rows come from the dispatch; group E is the shared expert, whose
 // rows TK + t are the tokens in order).
 //
-// This file holds the weight-streaming kernel ("stream"): one wavefront owns 16 output
-// columns of one group and walks the whole reduction axis once per 64-row chunk of the
-// group, so weights are read from HBM exactly once when a group has at most 64 rows -- the
-// decode regime, where the layer is bound by HBM bandwidth.  Each lane loads 64 contiguous
-// bytes of its weight row per 128-element step (16-byte loads) and the same k range of its
-// activation row; the four 16-byte pieces feed four v_mfma_f32_16x16x32_bf16.  The k index
-// inside a step is permuted identically for both operands, so the sum is unchanged.
+// This file holds the weight-streaming kernel ("stream"), for groups of up to 64 rows -- the
+// decode regime, where the layer is bound by HBM bandwidth.  A workgroup of four wavefronts
+// owns 64 output columns of one group; each wavefront owns 16 of them and reads its weight
+// rows from HBM exactly once per 64-row chunk of the group, straight into registers, one
+// 128-element step ahead of the MFMAs that consume them.  The activation rows of the chunk
+// (gathered x rows for GEMM-1, h rows for GEMM-2) are shared by the four wavefronts: each step
+// they are copied by LDS DMA into one of two 16 KB LDS buffers, one step ahead, so every
+// activation byte leaves L2 once per workgroup and the loads of a step are waited for with a
+// single count and barrier.  A step feeds four v_mfma_f32_16x16x32_bf16 per 16-row block (gate
+// and up each for GEMM-1).  The k index inside a step is permuted identically for both
+// operands (KLayout), so the sum is unchanged.
 // MFMA 16x16x32 bf16 operand layout: lane l supplies row/column (l % 16) and eight
 // consecutive k values of block (l / 16); result element v of lane l is row 4*(l/16)+v,
 // column l % 16.
@@ -29,16 +33,15 @@ namespace {
 
 enum { WF_BF16 = 0, WF_Q4 = 1 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float b) {
-    uint4 r;
-    uint32_t* rp = (uint32_t*)&r;
+    u32x4 r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float lo = __builtin_fmaf(s, (float)((w >> (8 * j)) & 0xFu), b);
         const float hi = __builtin_fmaf(s, (float)((w >> (8 * j + 4)) & 0xFu), b);
-        rp[j] = pack_bf16x2(lo, hi);
+        r[j] = pack_bf16x2(lo, hi);
     }
     return as_bf16x8(r);
 }
@@ -51,39 +54,36 @@ struct WRow {
     const bf16_t* b;   // offset row (WF_Q4)
 };
 
-// NP pieces of 8 k values starting at k (8*NP contiguous elements of the row)
+// k layout of one reduction step inside a wave.  Lane l (group q = l / 16) supplies, for the
+// step's i-th MFMA, the 8 k values starting at k0 + kq + i * PS.  bf16 rows: kq = 8 q, PS = 32,
+// so the 4 lanes of a row read 64 contiguous bytes per load instruction; 4-bit rows: kq = 32 q,
+// PS = 8, so a lane's codes for a step are one 16-byte word group.  A and B use the same layout.
+template <int WF>
+struct KLayout {
+    static constexpr int PS = WF == WF_BF16 ? 32 : 8;
+    static __device__ __forceinline__ int kq(int lane, int np) { return (lane >> 4) * (WF == WF_BF16 ? 8 : 8 * np); }
+};
+
+// NP pieces of 8 k values (see KLayout) starting at k
 template <int WF, int NP>
 __device__ __forceinline__ void load_w(const WRow& r, int k, bf16x8 (&out)[4]) {
     if constexpr (WF == WF_BF16) {
-        const uint4* p = (const uint4*)(r.w + k);
 #pragma unroll
-        for (int i = 0; i < NP; ++i) out[i] = as_bf16x8(p[i]);
+        for (int i = 0; i < NP; ++i) out[i] = as_bf16x8(*(const u32x4*)(r.w + k + i * KLayout<WF>::PS));
     } else {
         const float s = bf16_to_f32(r.s[k >> 6]);
         const float b = bf16_to_f32(r.b[k >> 6]);
         if constexpr (NP == 4) {
-            const uint4 w = *(const uint4*)(r.q + (k >> 3));
-            out[0] = dequant8(w.x, s, b);
-            out[1] = dequant8(w.y, s, b);
-            out[2] = dequant8(w.z, s, b);
-            out[3] = dequant8(w.w, s, b);
+            const u32x4 w = *(const u32x4*)(r.q + (k >> 3));
+            out[0] = dequant8(w[0], s, b);
+            out[1] = dequant8(w[1], s, b);
+            out[2] = dequant8(w[2], s, b);
+            out[3] = dequant8(w[3], s, b);
         } else {
             const uint2 w = *(const uint2*)(r.q + (k >> 3));
             out[0] = dequant8(w.x, s, b);
             out[1] = dequant8(w.y, s, b);
         }
-    }
-}
-
-template <int NP>
-__device__ __forceinline__ void load_a(const bf16_t* row, int k, bf16x8 (&out)[4]) {
-    if (row) {
-        const uint4* p = (const uint4*)(row + k);
-#pragma unroll
-        for (int i = 0; i < NP; ++i) out[i] = as_bf16x8(p[i]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < NP; ++i) out[i] = as_bf16x8(make_uint4(0, 0, 0, 0));
     }
 }
 
@@ -126,127 +126,158 @@ __device__ __forceinline__ WRow weight_row(const GroupedArgs& a, int sel, int32_
     return r;
 }
 
-// One reduction step of NP*32 k values (NP = 4 -> 128, NP = 2 -> 64) for GEMM-1.
+// k layout as 16-byte chunk indices inside a step: lane l's i-th piece of an NP-piece step
 template <int WF, int NP>
-__device__ __forceinline__ void step1(const WRow& rg, const WRow& ru, const bf16_t* const (&arow)[4], int nrb,
-                                      int k, f32x4 (&ag)[4], f32x4 (&au)[4]) {
-    bf16x8 bgv[4], buv[4];
-    load_w<WF, NP>(rg, k, bgv);
-    load_w<WF, NP>(ru, k, buv);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        if (rb >= nrb) break;
-        bf16x8 av[4];
-        load_a<NP>(arow[rb], k, av);
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            ag[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bgv[i], ag[rb], 0, 0, 0);
-            au[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], buv[i], au[rb], 0, 0, 0);
-        }
-    }
+__device__ __forceinline__ int piece_chunk(int lane, int i) {
+    return WF == WF_BF16 ? (lane >> 4) + 4 * i : NP * (lane >> 4) + i;
 }
 
-template <int WF, int NP>
-__device__ __forceinline__ void step2(const WRow& rd, const bf16_t* const (&arow)[4], int nrb, int k,
-                                      f32x4 (&ac)[4]) {
-    bf16x8 bv[4];
-    load_w<WF, NP>(rd, k, bv);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        if (rb >= nrb) break;
-        bf16x8 av[4];
-        load_a<NP>(arow[rb], k, av);
-#pragma unroll
-        for (int i = 0; i < NP; ++i) ac[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[i], ac[rb], 0, 0, 0);
-    }
-}
+constexpr int S_ROWS = 64;               // rows per chunk of a group
+constexpr int S_ROWB = 256;              // LDS bytes per activation row: one 128-element step
+constexpr int S_TILE = S_ROWS * S_ROWB;  // one LDS buffer
 
-// grid: x = ceil(max(I, Is) / 64) column blocks, y = groups [g0, g0 + gridDim.y)
-template <int WF>
-__global__ __launch_bounds__(256) void gemm1_stream(GroupedArgs a, int32_t g0) {
+// byte offset of 16-byte chunk c of row r in an activation buffer; the chunks of a row are
+// permuted by r mod 16, so the 16 rows a fragment read touches hit 16 different bank groups
+__device__ __forceinline__ uint32_t s_off(int r, int c) { return (uint32_t)(r * S_ROWB + ((c ^ (r & 15)) << 4)); }
+
+#define DSMOE_S_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Wait until this wave's vector-memory operations (register loads and LDS DMA) are complete,
+// then barrier: afterwards the step's activation buffer is filled for every wave.
+__device__ __forceinline__ void s_wait_all_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// GEMM-1 (G1): h = SwiGLU of x rows against W_gate / W_up;  GEMM-2: o = h rows against W_down.
+// grid: x = ceil(N / 64) column blocks (N = I or Is, resp. H), y = groups [g0, g0 + gridDim.y).
+// N is a multiple of 64 (bf16 and 4-bit layers), so every wave of a live workgroup has columns.
+template <int WF, bool G1>
+__global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
+    __shared__ __attribute__((aligned(1024))) char As[2 * S_TILE];
     const int32_t g = g0 + blockIdx.y;
     int32_t r0, cnt;
     group_rows(a, g, r0, cnt);
     if (cnt <= 0 || cnt > a.stream_max_rows) return;
     const bool shared = g == a.E;
-    const int32_t N = shared ? a.Is : a.I;
+    const int32_t N = G1 ? (shared ? a.Is : a.I) : a.H;   // output columns
+    const int32_t KD = G1 ? a.H : (shared ? a.Is : a.I);  // reduction length, a multiple of 64
+    if ((int32_t)blockIdx.x * 64 >= N) return;            // workgroup-uniform
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int32_t n0 = (blockIdx.x * 4 + wave) * 16;
-    if (n0 >= N) return;  // wave-uniform
-    const int32_t H = a.H;
-    const int32_t col = n0 + (lane & 15);
-    const WRow rg = weight_row<WF>(a, 0, g, shared, col, N, H);
-    const WRow ru = weight_row<WF>(a, 1, g, shared, col, N, H);
-    const bf16_t* x = (const bf16_t*)a.x;
-    bf16_t* h = (bf16_t*)a.h;
-    const int kq4 = (lane >> 4) * 32, kq2 = (lane >> 4) * 16;
-    const int32_t Hmain = H & ~127;
+    const int32_t col = blockIdx.x * 64 + wave * 16 + (lane & 15);
+    const WRow w0 = weight_row<WF>(a, G1 ? 0 : 2, g, shared, col, N, KD);
+    const WRow w1 = G1 ? weight_row<WF>(a, 1, g, shared, col, N, KD) : w0;
+    const bf16_t* abase = G1 ? (const bf16_t*)a.x : (const bf16_t*)a.h;
+    const int64_t lda = G1 ? a.H : a.ldh;
+    const int nfull = KD >> 7;       // 128-wide steps
+    const bool tail = (KD & 64) != 0;  // plus one 64-wide step
+    const int nsteps = nfull + (tail ? 1 : 0);  // >= 1
+    constexpr int NW = G1 ? 2 : 1;   // weight matrices
 
-    for (int32_t m0 = 0; m0 < cnt; m0 += 64) {
-        const int nrb = min(4, (cnt - m0 + 15) >> 4);
+    for (int32_t m0 = 0; m0 < cnt; m0 += S_ROWS) {
+        const int nrb = min(4, (cnt - m0 + 15) >> 4);  // live 16-row blocks
+        // LDS DMA sources: wave w fills rows [16 w, 16 w + 16) of the buffer (only for w < nrb),
+        // instruction j rows 16 w + 4 j + lane / 16; lane i writes chunk slot i % 16 of its row,
+        // which holds logical chunk (i % 16) ^ (row % 16)
         const bf16_t* arow[4];
+        int cj[4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int32_t rr = m0 + rb * 16 + (lane & 15);
-            arow[rb] = (rb < nrb && rr < cnt) ? x + (int64_t)row_token(a, r0 + rr) * H : nullptr;
+        for (int j = 0; j < 4; ++j) {
+            int32_t rr = m0 + wave * 16 + j * 4 + (lane >> 4);
+            rr = rr < cnt ? rr : cnt - 1;  // rows past the group are computed, never stored
+            const int64_t src = G1 ? (int64_t)row_token(a, r0 + rr) : (int64_t)(r0 + rr);
+            arow[j] = abase + src * lda;
+            cj[j] = (lane & 15) ^ (j * 4 + (lane >> 4));
         }
-        f32x4 ag[4], au[4];
+        auto issue_a = [&](int s, int buf) {
+            if (wave >= nrb) return;  // wave-uniform
+            const int32_t k = s << 7;
+            // the 64-wide tail step has chunks 0..7 only: the lanes of slots holding chunks 8..15
+            // fetch chunk c - 8 instead (in bounds, never read), so every lane of the DMA is active
+            const int cm = s == nfull ? 7 : 15;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) ag[rb] = au[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int32_t k = 0; k < Hmain; k += 128) step1<WF, 4>(rg, ru, arow, nrb, k + kq4, ag, au);
-        if (Hmain < H) step1<WF, 2>(rg, ru, arow, nrb, Hmain + kq2, ag, au);
+            for (int j = 0; j < 4; ++j)
+                __builtin_amdgcn_global_load_lds((const void*)(arow[j] + k + (cj[j] & cm) * 8),
+                                                 DSMOE_S_LDS(As + buf * S_TILE + (wave * 4 + j) * 1024), 16, 0, 0);
+        };
+        // weights of a full step (NP = 4) or of the tail step (NP = 2)
+        auto load_full = [&](int s, bf16x8 (&wv)[NW][4]) {
+            const int32_t k = (s << 7) + KLayout<WF>::kq(lane, 4);
+            load_w<WF, 4>(w0, k, wv[0]);
+            if (G1) load_w<WF, 4>(w1, k, wv[NW - 1]);
+        };
+        auto load_tail = [&](bf16x8 (&wv)[NW][4]) {
+            const int32_t k = (nfull << 7) + KLayout<WF>::kq(lane, 2);
+            load_w<WF, 2>(w0, k, wv[0]);
+            if (G1) load_w<WF, 2>(w1, k, wv[NW - 1]);
+        };
+        f32x4 acc[NW][4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            if (rb >= nrb) break;
+        for (int m = 0; m < NW; ++m)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int32_t rr = m0 + rb * 16 + (lane >> 4) * 4 + v;
-                if (rr < cnt) h[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(ag[rb][v]) * au[rb][v]);
+            for (int rb = 0; rb < 4; ++rb) acc[m][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](auto np_tag, int buf, const bf16x8 (&wv)[NW][4]) {
+            constexpr int NP = decltype(np_tag)::value;
+            const char* st = As + buf * S_TILE;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                if (rb >= nrb) break;
+                bf16x8 av[NP];
+#pragma unroll
+                for (int i = 0; i < NP; ++i)
+                    av[i] = __builtin_bit_cast(
+                        bf16x8, *(const u32x4*)(st + s_off(rb * 16 + (lane & 15), piece_chunk<WF, NP>(lane, i))));
+#pragma unroll
+                for (int i = 0; i < NP; ++i)
+#pragma unroll
+                    for (int m = 0; m < NW; ++m)
+                        acc[m][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], wv[m][i], acc[m][rb], 0, 0, 0);
             }
-        }
-    }
-}
+        };
 
-// grid: x = H / 64 column blocks, y = groups
-template <int WF>
-__global__ __launch_bounds__(256) void gemm2_stream(GroupedArgs a, int32_t g0) {
-    const int32_t g = g0 + blockIdx.y;
-    int32_t r0, cnt;
-    group_rows(a, g, r0, cnt);
-    if (cnt <= 0 || cnt > a.stream_max_rows) return;
-    const bool shared = g == a.E;
-    const int32_t KD = shared ? a.Is : a.I;  // reduction length
-    const int32_t H = a.H;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int32_t n0 = (blockIdx.x * 4 + wave) * 16;
-    if (n0 >= H) return;
-    const int32_t col = n0 + (lane & 15);
-    const WRow rd = weight_row<WF>(a, 2, g, shared, col, H, KD);
-    const bf16_t* h = (const bf16_t*)a.h;
-    bf16_t* o = (bf16_t*)a.o;
-    const int kq4 = (lane >> 4) * 32, kq2 = (lane >> 4) * 16;
-    const int32_t Kmain = KD & ~127;
+        // one full step: publish its activations, start the next step's loads, run its MFMAs
+        auto step = [&](int s, const bf16x8 (&cur)[NW][4], bf16x8 (&nxt)[NW][4]) {
+            s_wait_all_barrier();
+            if (s + 1 < nsteps) issue_a(s + 1, (s + 1) & 1);
+            if (s + 1 < nfull) load_full(s + 1, nxt);
+            compute(std::integral_constant<int, 4>{}, s & 1, cur);
+        };
 
-    for (int32_t m0 = 0; m0 < cnt; m0 += 64) {
-        const int nrb = min(4, (cnt - m0 + 15) >> 4);
-        const bf16_t* arow[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int32_t rr = m0 + rb * 16 + (lane & 15);
-            arow[rb] = (rb < nrb && rr < cnt) ? h + (int64_t)(r0 + rr) * a.ldh : nullptr;
+        __syncthreads();  // the previous chunk's reads of both buffers are done
+        bf16x8 wa[NW][4], wb[NW][4];
+        issue_a(0, 0);
+        if (nfull > 0) load_full(0, wa);
+        for (int s = 0; s < nfull; s += 2) {  // ping-pong between two register sets
+            step(s, wa, wb);
+            if (s + 1 < nfull) step(s + 1, wb, wa);
         }
-        f32x4 ac[4];
+        if (tail) {  // a 64-wide last step (reduction lengths of 64 mod 128 only): weights unprefetched
+            bf16x8 wt[NW][4];
+            load_tail(wt);
+            s_wait_all_barrier();
+            compute(std::integral_constant<int, 2>{}, nfull & 1, wt);
+        }
+        // The epilogue reads the accumulators right after the last MFMA, which may sit behind a
+        // branch (the 16-row blocks past nrb are skipped).  This compiler's hazard recognizer
+        // has been seen to read an accumulator at such a join without the MFMA-to-VALU wait
+        // states, so they are issued explicitly: every accumulator passes through an empty asm
+        // that follows the wait states in program order, so no read of it can come earlier.
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) ac[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int32_t k = 0; k < Kmain; k += 128) step2<WF, 4>(rd, arow, nrb, k + kq4, ac);
-        if (Kmain < KD) step2<WF, 2>(rd, arow, nrb, Kmain + kq2, ac);
+        for (int m = 0; m < NW; ++m)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                if (m | rb) asm volatile("" : "+a"(acc[m][rb]));
+
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
             if (rb >= nrb) break;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int32_t rr = m0 + rb * 16 + (lane >> 4) * 4 + v;
-                if (rr < cnt) o[(int64_t)(r0 + rr) * H + col] = f32_to_bf16(ac[rb][v]);
+                if (rr >= cnt) continue;
+                if (G1)
+                    ((bf16_t*)a.h)[(int64_t)(r0 + rr) * a.ldh + col] =
+                        f32_to_bf16(silu_f(acc[0][rb][v]) * acc[NW - 1][rb][v]);
+                else
+                    ((bf16_t*)a.o)[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[0][rb][v]);
             }
         }
     }
@@ -259,9 +290,9 @@ hipError_t launch_gemm1_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32
     const int32_t N = max(a.I, a.Is);
     const dim3 grid((N + 63) / 64, g1 - g0);
     if (wdt == MOE_Q4G64)
-        hipLaunchKernelGGL(gemm1_stream<WF_Q4>, grid, dim3(256), 0, s, a, g0);
+        hipLaunchKernelGGL((stream_gemm<WF_Q4, true>), grid, dim3(256), 0, s, a, g0);
     else
-        hipLaunchKernelGGL(gemm1_stream<WF_BF16>, grid, dim3(256), 0, s, a, g0);
+        hipLaunchKernelGGL((stream_gemm<WF_BF16, true>), grid, dim3(256), 0, s, a, g0);
     return hipGetLastError();
 }
 
@@ -269,9 +300,9 @@ hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32
     if (g1 <= g0) return hipSuccess;
     const dim3 grid((a.H + 63) / 64, g1 - g0);
     if (wdt == MOE_Q4G64)
-        hipLaunchKernelGGL(gemm2_stream<WF_Q4>, grid, dim3(256), 0, s, a, g0);
+        hipLaunchKernelGGL((stream_gemm<WF_Q4, false>), grid, dim3(256), 0, s, a, g0);
     else
-        hipLaunchKernelGGL(gemm2_stream<WF_BF16>, grid, dim3(256), 0, s, a, g0);
+        hipLaunchKernelGGL((stream_gemm<WF_BF16, false>), grid, dim3(256), 0, s, a, g0);
     return hipGetLastError();
 }
 

@@ -326,8 +326,9 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
 // global_load_lds_dwordx4 moves 16 bytes per lane straight into LDS (lane i of an instruction
 // fills bytes [16 i, 16 i + 16) of a 1 KB block), so no staging registers are needed and three
 // k-stages of 32 can be in flight while the matrix cores work on the fourth.  LDS rows are 64
-// bytes (32 bf16); the four 16-byte chunks of row r sit at chunk c ^ ((r >> 1) & 3), which makes
-// the eight lanes of each ds_read_b128 phase hit eight distinct 16-byte bank groups.  A lane of a
+// bytes (32 bf16); the four 16-byte chunks of row r sit at chunk c ^ (((r >> 1) ^ (r >> 2)) & 3),
+// which makes the lanes of each ds_read_b128 phase (8 or 16 consecutive rows) hit distinct
+// 16-byte bank groups.  A lane of a
 // DMA instruction therefore fetches the logical chunk that its LDS slot holds.  The compiler
 // does not track these LDS writes, so the waits are explicit: before stage s is read, each wave
 // waits until at most the later stages' loads are outstanding (vmcnt) and then meets the others
@@ -335,17 +336,33 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
 // the previous iteration.
 // ---------------------------------------------------------------------------------------------
 namespace dma {
-constexpr int BKD = 32;        // k per stage
-constexpr int ROWB = 64;       // bytes per LDS row
-constexpr int NST = 4;         // ring depth
-__device__ __forceinline__ uint32_t off(int r, int c) { return (uint32_t)(r * ROWB + ((c ^ ((r >> 1) & 3)) << 4)); }
+constexpr int BKD = 64;        // k per stage: a whole 128-byte line of every row
+constexpr int ROWB = 128;      // bytes per LDS row
+constexpr int NST = 2;         // ring depth
+constexpr int LDS_MAX = 160 * 1024;
+constexpr int ring_bytes(int bm) { return NST * (bm + 256) * ROWB; }
+// chunk swizzle: the 8 chunks of row r are permuted by (r ^ r/8) mod 8, which keeps the MFMA
+// operand reads free of bank conflicts whether a ds_read_b128 phase serves 8 lanes (rows r..r+7)
+// or 16 lanes (rows r..r+15)
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ uint32_t off(int r, int c) { return (uint32_t)(r * ROWB + ((c ^ swz(r)) << 4)); }
 }  // namespace dma
 
 #define DSMOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// Wait until at most N vector-memory operations of this wave are outstanding and its LDS reads
+// have returned, then barrier.  The LDS DMA writes are invisible to the compiler's own wait
+// insertion, hence the explicit counts.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// wait until at most `later` stages of D loads each are outstanding, then barrier
+template <int D>
+__device__ __forceinline__ void wait_stages(int later) {
+    if (later <= 0) wait_vm_barrier<0>();
+    else wait_vm_barrier<D>();
 }
 
 template <int BM, bool SWIGLU>
@@ -357,6 +374,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
     constexpr int A_DMA = A_BYTES / 1024 / 4;  // DMA instructions per wave per stage
     constexpr int B_DMA = B_BYTES / 1024 / 4;
     constexpr int D = A_DMA + B_DMA;
+    static_assert(ring_bytes(BM) <= LDS_MAX, "ring exceeds LDS");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const GroupedArgs& a = ta.a;
@@ -382,13 +400,14 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- DMA sources: instruction j of this wave fills LDS rows [16 (wave*X + j), +16) -----
+    // ---- DMA sources: instruction j of this wave fills LDS rows [8 (wave*X + j), +8); lane i
+    // writes chunk i % 8 of row i / 8, so it fetches the logical chunk that the swizzle puts there
     const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
     uint32_t a_off[A_DMA];
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
-        const int r = (wave * A_DMA + j) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 1) & 3);
+        const int r = (wave * A_DMA + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
         int32_t rr = m0 + r;
         rr = rr < cnt ? rr : cnt - 1;  // rows past the group are computed, never stored
         const int32_t row = r0 + rr;
@@ -412,15 +431,15 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
     uint32_t b_off[B_DMA];
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
-        const int br = (wave * B_DMA + j) * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ ((br >> 1) & 3);
+        const int br = (wave * B_DMA + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(br);
         int32_t n = n0 + (SWIGLU ? br % (NB / 2) : br);
         n = n < N ? n : N - 1;  // columns past N are computed, never stored
         b_off[j] = (uint32_t)n * (uint32_t)KD + c * 8;
     }
-    // a wave's B instruction j covers 16 rows, all gate or all up (NB/2 is a multiple of 16)
+    // a wave's B instruction j covers 8 rows, all gate or all up (NB/2 is a multiple of 8)
     auto issue = [&](int kt) {
-        char* st = smem + (kt & (NST - 1)) * ST_BYTES;
+        char* st = smem + (kt % NST) * ST_BYTES;
         const int32_t k0 = kt * BKD;
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
@@ -428,7 +447,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
                                              DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < B_DMA; ++j) {
-            const int br0 = (wave * B_DMA + j) * 16;
+            const int br0 = (wave * B_DMA + j) * 8;
             const bf16_t* wb = (SWIGLU && br0 >= NB / 2) ? wb1 : wb0;
             __builtin_amdgcn_global_load_lds((const void*)(wb + b_off[j] + k0),
                                              DSMOE_LDS_PTR(st + A_BYTES + (wave * B_DMA + j) * 1024), 16, 0, 0);
@@ -444,43 +463,53 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) brow[j] = SWIGLU ? (j < 2 ? 0 : NB / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
 
-    const int nk = KD / BKD;  // >= 2
-    issue(0);
-    issue(1);
-    if (nk > 2) issue(2);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int ahead = min(nk - 1 - kt, 2);
-        if (ahead == 2)
-            wait_vm_barrier<2 * D>();
-        else if (ahead == 1)
-            wait_vm_barrier<D>();
-        else
-            wait_vm_barrier<0>();
-        if (kt + 3 < nk) issue(kt + 3);
-        const char* st = smem + (kt & (NST - 1)) * ST_BYTES;
-        // all operand fragments of the stage first, then the MFMAs: only the first MFMA waits
-        // for LDS, the remaining reads land while the matrix cores are busy
-        constexpr int KS = BKD / 16;
-        bf16x8 af[KS][MT], bfr[KS][4];
+    // Software pipeline over k16 steps (four per stage): the fragments of the next step are read
+    // from LDS while the current step's MFMAs run.  The wait + barrier that publishes stage kt+1
+    // sits before the last step of stage kt; once every wave has passed it, the fragments of
+    // stage kt are all in registers, so its slot is refilled with stage kt+NST right away and
+    // those loads have the next four steps to land.
+    const int nk = KD / BKD;  // >= 1
+    bf16x8 fa[2][MT], fb[2][4];
+    auto read_frags = [&](int kt, int s, int buf) {
+        const char* st = smem + (kt % NST) * ST_BYTES;
+        const int c = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int c = 2 * s + (lane >> 5);
+        for (int j = 0; j < 4; ++j)
+            fb[buf][j] = as_bf16x8(*(const u32x4*)(st + A_BYTES + off(brow[j] + (lane & 31), c)));
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[s][j] = as_bf16x8(*(const u32x4*)(st + A_BYTES + off(brow[j] + (lane & 31), c)));
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-                af[s][i] = as_bf16x8(*(const u32x4*)(st + off(wm * WM + i * 32 + (lane & 31), c)));
+        for (int i = 0; i < MT; ++i) fa[buf][i] = as_bf16x8(*(const u32x4*)(st + off(wm * WM + i * 32 + (lane & 31), c)));
+    };
+    // one k16 step: its first MFMA, then (optionally) the next step's fragment reads, then the
+    // remaining MFMAs -- pinned in that order so each LDS read issues under a running MFMA
+    auto mfma_step = [&](int buf, bool then_read, int rkt, int rs, int rbuf) {
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][0], fb[buf][0], acc[0][0], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (then_read) {
+            read_frags(rkt, rs, rbuf);
+            __builtin_amdgcn_sched_group_barrier(0x100, MT + 4, 0);
         }
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, KS * (MT + 4), 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, KS * MT * 4, 0);    // MFMAs
+            for (int j = 0; j < 4; ++j)
+                if (i | j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MT * 4 - 1, 0);
+    };
+    const int pro = min(nk, NST);  // stages issued up front
+    for (int j = 0; j < pro; ++j) issue(j);
+    wait_stages<D>(pro - 1);
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        mfma_step(0, true, kt, 1, 1);
+        mfma_step(1, true, kt, 2, 0);
+        mfma_step(0, true, kt, 3, 1);
+        const bool next = kt + 1 < nk;
+        if (next) {
+            // issued so far: stages < min(nk, kt + NST); wait for kt+1, let the later ones fly
+            wait_stages<D>(min(nk, kt + NST) - (kt + 2));
+            if (kt + NST < nk) issue(kt + NST);
+        }
+        mfma_step(1, next, kt + 1, 0, 0);
     }
 
     const int col_l = lane & 31, rgrp = (lane >> 5) * 4;
@@ -560,7 +589,7 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
 
 template <int BM, bool SW>
 hipError_t launch_dma_t(const TileArgs& ta, hipStream_t s) {
-    const size_t lds = (size_t)dma::NST * (BM + NB) * dma::ROWB;
+    const size_t lds = (size_t)dma::ring_bytes(BM);
     const unsigned grid = (unsigned)(((ta.nwg + 7) / 8) * 8);
     hipLaunchKernelGGL((gemm_dma<BM, SW>), dim3(grid), dim3(THREADS), lds, s, ta);
     return hipGetLastError();
@@ -583,7 +612,7 @@ int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM) {
 
 // largest dynamic LDS any tiled kernel of this tile height uses
 int32_t tiled_lds_bytes(int32_t BM) {
-    const int32_t reg_staged = 2 * (BM + NB) * 128, dma_ring = dma::NST * (BM + NB) * dma::ROWB;
+    const int32_t reg_staged = 2 * (BM + NB) * 128, dma_ring = dma::ring_bytes(BM);
     return reg_staged > dma_ring ? reg_staged : dma_ring;
 }
 
