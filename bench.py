@@ -194,7 +194,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3"])
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4"])
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode batch")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     args = ap.parse_args()
@@ -221,7 +221,7 @@ def main():
     w = main_res["w"]
     sec = None
     if not args.no_secondary:
-        other = "c2" if args.workload == "c3" else "c3"
+        other = "c3" if args.workload == "c2" else "c2"
         sec = run_workload(other, max(args.steps, 20) if other == "c2" else args.steps, args.warmup, cache)
 
     def summary(res):
@@ -239,8 +239,10 @@ def main():
             ach = tiled_gemm1_flops(wl, res["counts"]) / (res["gemm1_ms"] / 1e3) / 1e12
             roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
-                    "kernel": "gemm_dma<256, true> (tiled gate/up + SwiGLU: groups above 64 rows and the "
-                              "shared expert)"}
+                    "kernel": ("gemm_dma<256, true> (tiled gate/up + SwiGLU: groups above 64 rows and the "
+                               "shared expert)") if wl.expert == "bf16" else
+                              ("tiled gate/up + SwiGLU kernels: gemm_tiled<BM, true, q4> for the 4-bit routed "
+                               "groups above 64 rows, gemm_dma<BM, true> for the bf16 shared expert")}
             layer = layer_flops(wl) / (res["step_ms"] / 1e3) / 1e12
             roof["layer_achieved"] = layer
             roof["layer_frac"] = layer / PEAK_BF16_TFLOPS
@@ -254,7 +256,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{w.name}: DeepSeek-V3-shaped {'prefill' if w.T > 256 else 'decode'} batch, "
                                f"T={w.T} H={w.H} E={w.E} top_k={w.K} n_group={w.G} topk_group={w.TG} "
-                               f"I={w.I} shared I={w.Is}, bf16" + (f", Zipf s={w.zipf_s} expert load"
+                               f"I={w.I} shared I={w.Is}, bf16 activations, {w.expert} routed experts"
+                               + (f", Zipf s={w.zipf_s} expert load"
                                                                     if w.zipf_s else ""),
                    "global_batch": w.T, "experts_hit": main_res["n_hit"], "max_expert_load": main_res["max_load"],
                    "parallelism": "single GPU"},

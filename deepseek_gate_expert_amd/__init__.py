@@ -58,6 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with `python -m deepseek_gate_expert_amd.build`")
+        # PyTorch ships its own HIP runtime with the same soname as the system one; loading torch
+        # first makes the library bind to that runtime, so both share one device context.  (Loaded
+        # the other way round, torch would pick up the system runtime and the library's launches
+        # would not reach the device torch uses.)
+        import torch  # noqa: F401
         lib = ctypes.CDLL(path)
         p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         lib.moe_strerror.restype = ctypes.c_char_p

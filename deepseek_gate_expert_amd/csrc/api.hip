@@ -7,8 +7,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "dsmoe_internal.hpp"
 
 using namespace dsmoe;
@@ -49,7 +47,9 @@ struct TilePlan {
     int32_t max_tiles;
 };
 
-// Shapes-only decision (no device reads): tiles of 256 rows when the average group is large.
+// Shapes-only decision (no device reads): tiles of 256 rows when the average group is large
+// (bf16 weights only: the 4-bit kernel keeps its dequantised operands in registers and runs
+// 128-row tiles).
 TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     TilePlan p{false, 128, 0};
     if (d->act_dtype != MOE_BF16 || d->T <= STREAM_MAX_ROWS) return p;
@@ -59,7 +59,7 @@ TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     if (d->T * (int64_t)d->H >= ((int64_t)1 << 32) || rows * ldh >= ((int64_t)1 << 32)) return p;
     p.on = true;
     const int64_t avg = d->T * d->route.top_k / d->E;
-    p.BM = (allow256 && avg >= 192) ? 256 : 128;
+    p.BM = (allow256 && avg >= 192 && d->expert_dtype == MOE_BF16) ? 256 : 128;
     p.max_tiles = tiled_max_tiles(d->T, d->route.top_k, d->E, p.BM);
     return p;
 }
@@ -135,45 +135,6 @@ int tiled_state() {
         g_tiled_state[dev] = st;
     }
     return g_tiled_state[dev];
-}
-
-// A library-owned stream (default priority, non-blocking) on which the weight-streaming
-// kernels of the small groups run while the tiled kernels of the large groups run on the
-// caller's stream: the first kind is bound by HBM bandwidth, the second by the matrix cores, and
-// the two touch disjoint rows of h and o.  One per (device, caller stream), created on first use
-// together with its fork/join events and kept until the process ends; when the table is full
-// or creation fails, the forward runs everything on the caller's stream.
-struct SideStream {
-    int dev;
-    hipStream_t user;
-    hipStream_t side;
-    hipEvent_t fork, join;
-};
-constexpr int MAX_SIDE = 64;
-std::mutex g_side_mu;
-SideStream g_side[MAX_SIDE];
-int g_nside = 0;
-
-const SideStream* side_stream(hipStream_t user) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    for (int i = 0; i < g_nside; ++i)
-        if (g_side[i].dev == dev && g_side[i].user == user) return &g_side[i];
-    if (g_nside == MAX_SIDE) return nullptr;
-    SideStream e{dev, user, nullptr, nullptr, nullptr};
-    bool ok = hipStreamCreateWithFlags(&e.side, hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&e.fork, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&e.join, hipEventDisableTiming) == hipSuccess;
-    if (!ok) {
-        if (e.join) (void)hipEventDestroy(e.join);
-        if (e.fork) (void)hipEventDestroy(e.fork);
-        if (e.side) (void)hipStreamDestroy(e.side);
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    g_side[g_nside] = e;
-    return &g_side[g_nside++];
 }
 
 // measurement hook state (see moe_set_stage_events)
@@ -360,18 +321,15 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
         if (ts != 3) tp = plan_tiles(d, ts == 1);
     }
     a.stream_max_rows = tp.on ? STREAM_MAX_ROWS : 0x7fffffff;
-    // with tiles on, the streaming kernels go to the side stream (when there is one)
-    const SideStream* side = tp.on ? side_stream(s) : nullptr;
-    const hipStream_t ss = side ? side->side : s;
     const int32_t rdt = q4 ? MOE_Q4G64 : MOE_BF16;
     const int32_t split = q4 ? E : gend;  // 4-bit routed groups vs bf16 (shared) group
     // weight-streaming kernels of one expert-GEMM pass (groups of at most stream_max_rows rows)
     auto streamed = [&](bool first) -> int {
-        if (f32) return hip_rc(first ? launch_gemm1_f32(a, ss) : launch_gemm2_f32(a, ss));
-        int r = hip_rc(first ? launch_gemm1_bf16(a, 0, split, rdt, ss) : launch_gemm2_bf16(a, 0, split, rdt, ss));
+        if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));
+        int r = hip_rc(first ? launch_gemm1_bf16(a, 0, split, rdt, s) : launch_gemm2_bf16(a, 0, split, rdt, s));
         if (!r && split < gend)
-            r = hip_rc(first ? launch_gemm1_bf16(a, split, gend, MOE_BF16, ss)
-                             : launch_gemm2_bf16(a, split, gend, MOE_BF16, ss));
+            r = hip_rc(first ? launch_gemm1_bf16(a, split, gend, MOE_BF16, s)
+                             : launch_gemm2_bf16(a, split, gend, MOE_BF16, s));
         return r;
     };
     // tiled kernels of one pass (the other groups)
@@ -384,25 +342,17 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
         return r;
     };
     if (tp.on && (rc = hip_rc(launch_tiles(a, tp.BM, STREAM_MAX_ROWS, tile_count, tile_info, s)))) return rc;
-    if (side) {
-        // fork: the side stream starts after dispatch; GEMM-2 of a small group follows its
-        // GEMM-1 in side-stream order
-        if ((rc = hip_rc(hipEventRecord(side->fork, s)))) return rc;
-        if ((rc = hip_rc(hipStreamWaitEvent(ss, side->fork, 0)))) return rc;
-        if ((rc = streamed(true))) return rc;
-        if ((rc = streamed(false))) return rc;
-        if ((rc = hip_rc(hipEventRecord(side->join, ss)))) return rc;
+    // With tiles on, the GEMM1 / GEMM2 stage events bracket the tiled kernels only (the
+    // dominant kernels of prefill layers); the streaming kernels run right before them.
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool first = pass == 0;
+        const int32_t stage = first ? MOE_STAGE_GEMM1 : MOE_STAGE_GEMM2;
+        if (!tp.on && (rc = hip_rc(mark(stage, 0, s)))) return rc;
+        if ((rc = streamed(first))) return rc;
+        if (tp.on && (rc = hip_rc(mark(stage, 0, s)))) return rc;
+        if ((rc = tiled(first))) return rc;
+        if ((rc = hip_rc(mark(stage, 1, s)))) return rc;
     }
-    if ((rc = hip_rc(mark(MOE_STAGE_GEMM1, 0, s)))) return rc;
-    if (!side && (rc = streamed(true))) return rc;
-    if ((rc = tiled(true))) return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_GEMM1, 1, s)))) return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_GEMM2, 0, s)))) return rc;
-    if (!side && (rc = streamed(false))) return rc;
-    if ((rc = tiled(false))) return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_GEMM2, 1, s)))) return rc;
-    // join before the combine reads o
-    if (side && (rc = hip_rc(hipStreamWaitEvent(s, side->join, 0)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 0, s)))) return rc;
     if ((rc = hip_rc(launch_combine(a, d->act_dtype, scores, slot_row, y, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 1, s)))) return rc;

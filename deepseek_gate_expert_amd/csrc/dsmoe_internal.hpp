@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/dsmoe.h"
+#include "dsmoe.h"  // include/ is on the include path
 
 namespace dsmoe {
 

@@ -64,25 +64,41 @@ struct KLayout {
     static __device__ __forceinline__ int kq(int lane, int np) { return (lane >> 4) * (WF == WF_BF16 ? 8 : 8 * np); }
 };
 
-// NP pieces of 8 k values (see KLayout) starting at k
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One weight row's operands for one step, as loaded: bf16 pieces, or 4-bit codes plus the
+// row's scale and offset for the step's quantisation group (dequantised only when used, so the
+// loads can run ahead of the MFMAs).
+template <int WF>
+struct WRegs;
+template <>
+struct WRegs<WF_BF16> {
+    bf16x8 v[4];
+    __device__ __forceinline__ bf16x8 frag(int i) const { return v[i]; }
+};
+template <>
+struct WRegs<WF_Q4> {
+    u32x4 q;
+    bf16_t s, b;
+    __device__ __forceinline__ bf16x8 frag(int i) const { return dequant8(q[i], bf16_to_f32(s), bf16_to_f32(b)); }
+};
+
+// NP pieces of 8 k values (see KLayout) starting at k.  Vector-memory operations issued: NP
+// 16-byte loads (bf16), or codes + scale + offset = 3 (4-bit).
 template <int WF, int NP>
-__device__ __forceinline__ void load_w(const WRow& r, int k, bf16x8 (&out)[4]) {
+__device__ __forceinline__ void load_w(const WRow& r, int k, WRegs<WF>& out) {
     if constexpr (WF == WF_BF16) {
 #pragma unroll
-        for (int i = 0; i < NP; ++i) out[i] = as_bf16x8(*(const u32x4*)(r.w + k + i * KLayout<WF>::PS));
+        for (int i = 0; i < NP; ++i) out.v[i] = as_bf16x8(*(const u32x4*)(r.w + k + i * KLayout<WF>::PS));
     } else {
-        const float s = bf16_to_f32(r.s[k >> 6]);
-        const float b = bf16_to_f32(r.b[k >> 6]);
+        out.s = r.s[k >> 6];
+        out.b = r.b[k >> 6];
         if constexpr (NP == 4) {
-            const u32x4 w = *(const u32x4*)(r.q + (k >> 3));
-            out[0] = dequant8(w[0], s, b);
-            out[1] = dequant8(w[1], s, b);
-            out[2] = dequant8(w[2], s, b);
-            out[3] = dequant8(w[3], s, b);
+            out.q = *(const u32x4*)(r.q + (k >> 3));
         } else {
-            const uint2 w = *(const uint2*)(r.q + (k >> 3));
-            out[0] = dequant8(w.x, s, b);
-            out[1] = dequant8(w.y, s, b);
+            const u32x2 w = *(const u32x2*)(r.q + (k >> 3));
+            out.q[0] = w[0];
+            out.q[1] = w[1];
         }
     }
 }
@@ -146,6 +162,10 @@ __device__ __forceinline__ uint32_t s_off(int r, int c) { return (uint32_t)(r * 
 // then barrier: afterwards the step's activation buffer is filled for every wave.
 __device__ __forceinline__ void s_wait_all_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Same, but the newest N operations (the next step's weight loads) may stay in flight.
+template <int N>
+__device__ __forceinline__ void s_wait_barrier() { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory"); }
+
 // GEMM-1 (G1): h = SwiGLU of x rows against W_gate / W_up;  GEMM-2: o = h rows against W_down.
 // grid: x = ceil(N / 64) column blocks (N = I or Is, resp. H), y = groups [g0, g0 + gridDim.y).
 // N is a multiple of 64 (bf16 and 4-bit layers), so every wave of a live workgroup has columns.
@@ -198,12 +218,13 @@ __global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
                                                  DSMOE_S_LDS(As + buf * S_TILE + (wave * 4 + j) * 1024), 16, 0, 0);
         };
         // weights of a full step (NP = 4) or of the tail step (NP = 2)
-        auto load_full = [&](int s, bf16x8 (&wv)[NW][4]) {
+        using W = WRegs<WF>;
+        auto load_full = [&](int s, W (&wv)[NW]) {
             const int32_t k = (s << 7) + KLayout<WF>::kq(lane, 4);
             load_w<WF, 4>(w0, k, wv[0]);
             if (G1) load_w<WF, 4>(w1, k, wv[NW - 1]);
         };
-        auto load_tail = [&](bf16x8 (&wv)[NW][4]) {
+        auto load_tail = [&](W (&wv)[NW]) {
             const int32_t k = (nfull << 7) + KLayout<WF>::kq(lane, 2);
             load_w<WF, 2>(w0, k, wv[0]);
             if (G1) load_w<WF, 2>(w1, k, wv[NW - 1]);
@@ -213,9 +234,14 @@ __global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
         for (int m = 0; m < NW; ++m)
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) acc[m][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        auto compute = [&](auto np_tag, int buf, const bf16x8 (&wv)[NW][4]) {
+        auto compute = [&](auto np_tag, int buf, const W (&wv)[NW]) {
             constexpr int NP = decltype(np_tag)::value;
             const char* st = As + buf * S_TILE;
+            bf16x8 wf[NW][NP];
+#pragma unroll
+            for (int m = 0; m < NW; ++m)
+#pragma unroll
+                for (int i = 0; i < NP; ++i) wf[m][i] = wv[m].frag(i);
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
                 if (rb >= nrb) break;
@@ -228,28 +254,44 @@ __global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
                 for (int i = 0; i < NP; ++i)
 #pragma unroll
                     for (int m = 0; m < NW; ++m)
-                        acc[m][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], wv[m][i], acc[m][rb], 0, 0, 0);
+                        acc[m][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], wf[m][i], acc[m][rb], 0, 0, 0);
             }
         };
 
-        // one full step: publish its activations, start the next step's loads, run its MFMAs
-        auto step = [&](int s, const bf16x8 (&cur)[NW][4], bf16x8 (&nxt)[NW][4]) {
-            s_wait_all_barrier();
-            if (s + 1 < nsteps) issue_a(s + 1, (s + 1) & 1);
-            if (s + 1 < nfull) load_full(s + 1, nxt);
+        // One full step: publish its activations, start the later steps' loads, run its MFMAs.
+        // Weights run two steps ahead in three rotating register sets; per wave the issue order
+        // is A(s+1), W(s+2) during step s, so at the top of step s everything but W(s+1) (the
+        // last WL operations) must have landed.  Past the end the loads repeat the last step
+        // (L2 hits, never consumed) instead of being skipped: with the same load sequence on
+        // every path the compiler's own waits for the weight registers stay exact rather than
+        // falling back to waiting for everything.
+        constexpr int WL = NW * (WF == WF_BF16 ? 4 : 3);  // vector-memory operations of one load_full
+        auto step = [&](int s, const W (&cur)[NW], W (&nxt2)[NW]) {
+            s_wait_barrier<WL>();
+            // the buffer written here was last read in step s-1; past the last step it is not
+            // read again in this chunk
+            issue_a(min(s + 1, nsteps - 1), (s + 1) & 1);
+            load_full(min(s + 2, nfull - 1), nxt2);
             compute(std::integral_constant<int, 4>{}, s & 1, cur);
         };
 
         __syncthreads();  // the previous chunk's reads of both buffers are done
-        bf16x8 wa[NW][4], wb[NW][4];
+        W wa[NW], wb[NW], wc[NW];
         issue_a(0, 0);
-        if (nfull > 0) load_full(0, wa);
-        for (int s = 0; s < nfull; s += 2) {  // ping-pong between two register sets
-            step(s, wa, wb);
-            if (s + 1 < nfull) step(s + 1, wb, wa);
+        if (nfull > 0) {
+            // both prologue loads are unconditional (with one full step the second repeats step 0
+            // and is never used), so the compiler's own wait before the loop's first MFMAs sees
+            // the same load order on entry as around the loop and stays exact
+            load_full(0, wa);
+            load_full(nfull > 1 ? 1 : 0, wb);
+            for (int s = 0; s < nfull; s += 3) {  // rotate through three register sets
+                step(s, wa, wc);
+                if (s + 1 < nfull) step(s + 1, wb, wa);
+                if (s + 2 < nfull) step(s + 2, wc, wb);
+            }
         }
         if (tail) {  // a 64-wide last step (reduction lengths of 64 mod 128 only): weights unprefetched
-            bf16x8 wt[NW][4];
+            W wt[NW];
             load_tail(wt);
             s_wait_all_barrier();
             compute(std::integral_constant<int, 2>{}, nfull & 1, wt);

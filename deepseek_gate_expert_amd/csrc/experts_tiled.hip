@@ -8,14 +8,9 @@
 //   * a workgroup (4 waves) computes a BM x 256 tile: BM rows of one group against 256 rows of
 //     weights -- for GEMM-1 the gate and up rows of the same 128 output columns, for GEMM-2 256
 //     rows of W_down -- with v_mfma_f32_32x32x16_bf16 and fp32 accumulators;
-//   * A (gathered activation rows, or the contiguous h rows) and B (weights) are staged through
-//     LDS in k-steps of 64 with two buffers: the global loads of step s+1 are in flight while
-//     step s runs on the matrix cores; one barrier per step;
-//   * LDS rows are 128 bytes (64 bf16); the eight 16-byte chunks of a row are XOR-swizzled with
-//     the row index so that both the staging writes and the MFMA operand reads are free of bank
-//     conflicts;
-//   * 4-bit weights are dequantised (bf16(s*q + b)) once per LDS tile while staging, so the cost
-//     is amortised over the BM rows of the tile;
+//   * operands reach LDS by direct-to-LDS DMA in k-stages of 64 (one 128-byte line per row),
+//     through a ring of stages, with one barrier per stage (gemm_dma); 4-bit weights skip LDS and
+//     are dequantised in registers (gemm_dma_q4);
 //   * the list of (group, first row) tiles is built on the device from the dispatch offsets, so
 //     no count ever returns to the host; the grid is an upper bound and surplus workgroups exit;
 //   * workgroup ids are remapped so that the workgroups an XCD receives (ids congruent mod 8)
@@ -23,22 +18,17 @@
 //
 // MFMA 32x32x16 bf16 layout: lane l supplies row/column (l % 32) and the 8 k values of chunk
 // (l / 32) of each 16-k step; result element v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
-// column l % 32.
+// column l % 32.  Which 8 k values a chunk holds is free as long as both operands agree.
 #include "dsmoe_internal.hpp"
 
 namespace dsmoe {
 namespace {
 
-enum { WF_BF16 = 0, WF_Q4 = 1 };
-
-constexpr int BK = 64;        // k per LDS stage (one 4-bit scale group)
 constexpr int NB = 256;       // weight rows per tile
-constexpr int THREADS = 256;  // 4 waves, 2 x 2
+constexpr int THREADS = 256;  // 4 waves
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// byte offset of 16-byte chunk c of row r in a [rows][64] bf16 LDS tile
-__device__ __forceinline__ uint32_t lds_off(int r, int c) { return (uint32_t)(r * 128 + ((c ^ (r & 7)) << 4)); }
 
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float b) {
     u32x4 r;
@@ -86,254 +76,20 @@ __device__ __forceinline__ bool map_tile(const TileArgs& ta, int32_t& tile, int3
     return true;
 }
 
-// SWIGLU = true: GEMM-1 (gate/up + SwiGLU -> h); false: GEMM-2 (down -> o)
-template <int BM, bool SWIGLU, int WF>
-__global__ __launch_bounds__(THREADS) void gemm_tiled(TileArgs ta) {
-    constexpr int WM = BM / 2;          // rows per wave
-    constexpr int MT = WM / 32;         // 32-row MFMA tiles per wave
-    constexpr int A_LD = BM * 8 / THREADS;  // 16-byte A chunks staged per thread per step
-    constexpr int B_LD = NB * 8 / THREADS;  // 16-byte B chunks per thread per step (bf16)
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    // LDS: A buffers [2][BM][128 B], then B buffers [2][NB][128 B]
-    auto As = [&](int buf) -> char* { return smem + buf * (BM * 128); };
-    auto Bs = [&](int buf) -> char* { return smem + 2 * BM * 128 + buf * (NB * 128); };
-
-    const GroupedArgs& a = ta.a;
-    int32_t tile, ct;
-    if (!map_tile(ta, tile, ct)) return;
-    const int32_t g = ta.tile_info[2 * tile], m0 = ta.tile_info[2 * tile + 1];
-    if (g < ta.g0 || g >= ta.g1) return;
-    const bool shared = g == a.E;
-    int32_t r0, cnt;
-    if (!shared) {
-        r0 = a.offsets[g];
-        cnt = a.offsets[g + 1] - r0;
-    } else {
-        r0 = a.TK;
-        cnt = (int32_t)a.T;
-    }
-    const int32_t N = SWIGLU ? (shared ? a.Is : a.I) : a.H;       // output columns of this group
-    const int32_t KD = SWIGLU ? a.H : (shared ? a.Is : a.I);      // reduction length
-    constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
-    const int32_t n0 = ct * OUT_COLS;
-    if (n0 >= N) return;
-
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // ---- per-thread global sources: uniform 64-bit bases + 32-bit element offsets -----------
-    const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
-    uint32_t a_off[A_LD];
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int id = tid + THREADS * i;
-        int32_t rr = m0 + id / 8;
-        rr = rr < cnt ? rr : cnt - 1;  // clamp: rows past the group are computed, never stored
-        const int32_t row = r0 + rr;
-        const int c = id % 8;
-        if (SWIGLU) {
-            const int32_t tok = row < a.TK ? a.sorted_slot[row] / a.K : row - a.TK;
-            a_off[i] = (uint32_t)tok * (uint32_t)a.H + c * 8;
-        } else {
-            a_off[i] = (uint32_t)row * (uint32_t)a.ldh + c * 8;
-        }
-    }
-    // weight matrices of this group (uniform); B-tile row br maps to output column w_row(br),
-    // clamped to N - 1 past the last column (such columns are never stored)
-    const bf16_t *wb0 = nullptr, *wb1 = nullptr;   // bf16: gate/up (GEMM-1) or down (both = down)
-    const uint32_t *qb0 = nullptr, *qb1 = nullptr; // 4-bit codes
-    const bf16_t *sb0 = nullptr, *sb1 = nullptr, *zb0 = nullptr, *zb1 = nullptr;
-    {
-        const int32_t out_dim = SWIGLU ? a.I : a.H;
-        const int64_t eoff = (int64_t)g * out_dim;  // first row of this expert
-        if (WF == WF_BF16) {
-            if (SWIGLU) {
-                wb0 = shared ? (const bf16_t*)a.swg : (const bf16_t*)a.wg + eoff * KD;
-                wb1 = shared ? (const bf16_t*)a.swu : (const bf16_t*)a.wu + eoff * KD;
-            } else {
-                wb0 = wb1 = shared ? (const bf16_t*)a.swd : (const bf16_t*)a.wd + eoff * KD;
-            }
-        } else {
-            if (SWIGLU) {
-                qb0 = (const uint32_t*)a.wg + eoff * (KD / 8);
-                qb1 = (const uint32_t*)a.wu + eoff * (KD / 8);
-                sb0 = a.sg + eoff * (KD / 64);
-                sb1 = a.su + eoff * (KD / 64);
-                zb0 = a.bg + eoff * (KD / 64);
-                zb1 = a.bu + eoff * (KD / 64);
-            } else {
-                qb0 = qb1 = (const uint32_t*)a.wd + eoff * (KD / 8);
-                sb0 = sb1 = a.sd + eoff * (KD / 64);
-                zb0 = zb1 = a.bd + eoff * (KD / 64);
-            }
-        }
-    }
-    constexpr int QL = B_LD / 4;  // 4-bit: 16-byte code loads per thread per step
-    uint32_t b_off[WF == WF_BF16 ? B_LD : QL];
-    bool b_hi[WF == WF_BF16 ? B_LD : QL];  // row belongs to the second matrix (up)
-#pragma unroll
-    for (int i = 0; i < (WF == WF_BF16 ? B_LD : QL); ++i) {
-        const int id = tid + THREADS * i;
-        const int br = WF == WF_BF16 ? id / 8 : id / 2;
-        int32_t n = n0 + (SWIGLU ? br % (NB / 2) : br);
-        n = n < N ? n : N - 1;
-        b_hi[i] = SWIGLU && br >= NB / 2;
-        if (WF == WF_BF16)
-            b_off[i] = (uint32_t)n * (uint32_t)KD + (id % 8) * 8;
-        else
-            b_off[i] = (uint32_t)n * (uint32_t)(KD / 8) + (id % 2) * 4;  // word offset of the half row
-    }
-
-    // ---- staging registers --------------------------------------------------------------
-    u32x4 ra[A_LD];
-    u32x4 rb[WF == WF_BF16 ? B_LD : QL];
-    float rs[QL], rz[QL];
-
-    // ---- accumulators -------------------------------------------------------------------
-    // wave tile: WM rows x 128 weight rows = MT x 4 MFMA tiles of 32 x 32
-    f32x16 acc[MT][4];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-    // B-tile rows of this wave's 4 column tiles
-    int brow[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (SWIGLU)  // tiles 0,1: gate rows; 2,3: the matching up rows
-            brow[j] = (j < 2 ? 0 : NB / 2) + wn * 64 + (j & 1) * 32;
-        else
-            brow[j] = wn * 128 + j * 32;
-    }
-
-    const int nk = KD / BK;
-#define DSMOE_GLOAD(K0)                                                                       \
-    do {                                                                                      \
-        const int32_t k_ = (K0);                                                              \
-        _Pragma("unroll") for (int i = 0; i < A_LD; ++i) ra[i] = *(const u32x4*)(a_base + a_off[i] + k_); \
-        if constexpr (WF == WF_BF16) {                                                        \
-            _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                                  \
-                rb[i] = *(const u32x4*)((b_hi[i] ? wb1 : wb0) + b_off[i] + k_);               \
-        } else {                                                                              \
-            _Pragma("unroll") for (int i = 0; i < QL; ++i) {                                  \
-                const int br_ = (tid + THREADS * i) / 2;                                      \
-                int32_t n_ = n0 + (SWIGLU ? br_ % (NB / 2) : br_);                            \
-                n_ = n_ < N ? n_ : N - 1;                                                     \
-                const uint32_t so_ = (uint32_t)n_ * (uint32_t)(KD / 64) + k_ / 64;            \
-                rb[i] = *(const u32x4*)((b_hi[i] ? qb1 : qb0) + b_off[i] + k_ / 8);           \
-                rs[i] = bf16_to_f32((b_hi[i] ? sb1 : sb0)[so_]);                              \
-                rz[i] = bf16_to_f32((b_hi[i] ? zb1 : zb0)[so_]);                              \
-            }                                                                                 \
-        }                                                                                     \
-    } while (0)
-#define DSMOE_LSTORE(BUF)                                                                     \
-    do {                                                                                      \
-        char* as_ = As(BUF);                                                                  \
-        char* bs_ = Bs(BUF);                                                                  \
-        _Pragma("unroll") for (int i = 0; i < A_LD; ++i) {                                    \
-            const int id = tid + THREADS * i;                                                 \
-            *(u32x4*)(as_ + lds_off(id / 8, id % 8)) = ra[i];                                 \
-        }                                                                                     \
-        if constexpr (WF == WF_BF16) {                                                        \
-            _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                                \
-                const int id = tid + THREADS * i;                                             \
-                *(u32x4*)(bs_ + lds_off(id / 8, id % 8)) = rb[i];                             \
-            }                                                                                 \
-        } else {                                                                              \
-            _Pragma("unroll") for (int i = 0; i < QL; ++i) {                                  \
-                const int id = tid + THREADS * i;                                             \
-                const int br_ = id / 2, hf_ = id % 2;                                         \
-                *(u32x4*)(bs_ + lds_off(br_, hf_ * 4 + 0)) = dequant8(rb[i][0], rs[i], rz[i]); \
-                *(u32x4*)(bs_ + lds_off(br_, hf_ * 4 + 1)) = dequant8(rb[i][1], rs[i], rz[i]); \
-                *(u32x4*)(bs_ + lds_off(br_, hf_ * 4 + 2)) = dequant8(rb[i][2], rs[i], rz[i]); \
-                *(u32x4*)(bs_ + lds_off(br_, hf_ * 4 + 3)) = dequant8(rb[i][3], rs[i], rz[i]); \
-            }                                                                                 \
-        }                                                                                     \
-    } while (0)
-    DSMOE_GLOAD(0);
-    DSMOE_LSTORE(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) DSMOE_GLOAD((kt + 1) * BK);
-        const char* Ab = As(buf);
-        const char* Bb = Bs(buf);
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-            const int c = 2 * s + (lane >> 5);
-            bf16x8 af[MT], bfr[4];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const int r = wm * WM + i * 32 + (lane & 31);
-                af[i] = as_bf16x8(*(const u32x4*)(Ab + lds_off(r, c)));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = brow[j] + (lane & 31);
-                bfr[j] = as_bf16x8(*(const u32x4*)(Bb + lds_off(r, c)));
-            }
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) DSMOE_LSTORE(buf ^ 1);
-        __syncthreads();
-    }
-#undef DSMOE_GLOAD
-#undef DSMOE_LSTORE
-
-    // ---- epilogue -----------------------------------------------------------------------
-    const int col_l = lane & 31, rgrp = (lane >> 5) * 4;
-    if (SWIGLU) {
-        bf16_t* h = (bf16_t*)a.h;
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int32_t col = n0 + wn * 64 + j * 32 + col_l;
-                if (col >= N) continue;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int32_t rr = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                    if (rr < cnt)
-                        h[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 2][v]);
-                }
-            }
-    } else {
-        bf16_t* o = (bf16_t*)a.o;
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int32_t col = n0 + wn * 128 + j * 32 + col_l;
-                if (col >= N) continue;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int32_t rr = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                    if (rr < cnt) o[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[i][j][v]);
-                }
-            }
-    }
-}
-
-
 // ---------------------------------------------------------------------------------------------
-// bf16 weights: direct-to-LDS loads into a 4-stage ring.
+// bf16 weights: direct-to-LDS loads into a ring of 64-k stages.
 //
 // global_load_lds_dwordx4 moves 16 bytes per lane straight into LDS (lane i of an instruction
-// fills bytes [16 i, 16 i + 16) of a 1 KB block), so no staging registers are needed and three
-// k-stages of 32 can be in flight while the matrix cores work on the fourth.  LDS rows are 64
-// bytes (32 bf16); the four 16-byte chunks of row r sit at chunk c ^ (((r >> 1) ^ (r >> 2)) & 3),
-// which makes the lanes of each ds_read_b128 phase (8 or 16 consecutive rows) hit distinct
-// 16-byte bank groups.  A lane of a
-// DMA instruction therefore fetches the logical chunk that its LDS slot holds.  The compiler
-// does not track these LDS writes, so the waits are explicit: before stage s is read, each wave
-// waits until at most the later stages' loads are outstanding (vmcnt) and then meets the others
-// at a barrier; the slot refilled after that barrier is the one every wave finished reading in
-// the previous iteration.
+// fills bytes [16 i, 16 i + 16) of a 1 KB block), so no staging registers are needed.  A stage
+// holds 64 k of every row -- one whole 128-byte line, so each DMA instruction fetches 8 full
+// lines (fetching half lines per instruction measured about a third slower).  The eight 16-byte
+// chunks of row r sit at chunk c ^ ((r ^ r/8) & 7), which makes the lanes of each ds_read_b128
+// phase (8 or 16 consecutive rows) hit distinct 16-byte bank groups; a lane of a DMA instruction
+// therefore fetches the logical chunk that its LDS slot holds.  The compiler does not track
+// these LDS writes, so the waits are explicit: before stage s is read, each wave waits until at
+// most the later stages' loads are outstanding (vmcnt) and then meets the others at a barrier;
+// the slot refilled after that barrier is the one every wave finished reading.  The 2 x 2 waves
+// each own a 128-row x 128-weight-row quarter of the tile.
 // ---------------------------------------------------------------------------------------------
 namespace dma {
 constexpr int BKD = 64;        // k per stage: a whole 128-byte line of every row
@@ -363,6 +119,45 @@ template <int D>
 __device__ __forceinline__ void wait_stages(int later) {
     if (later <= 0) wait_vm_barrier<0>();
     else wait_vm_barrier<D>();
+}
+
+// Epilogue of a 32x32-MFMA tile: rows [mrow, mrow + 32 MT) of the group, the wave's output
+// columns.  GEMM-1 holds gate accumulators in j = 0, 1 and up in j = 2, 3 (64 output columns
+// per wave) and writes bf16(silu(gate) * up) to h; GEMM-2 writes its 128 columns to o.
+template <int MT, bool SWIGLU>
+__device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16 (&acc)[MT][4], int32_t r0,
+                                              int32_t cnt, int32_t mrow, int32_t n0, int32_t N, int wn, int lane) {
+    const int col_l = lane & 31, rgrp = (lane >> 5) * 4;
+    if (SWIGLU) {
+        bf16_t* h = (bf16_t*)a.h;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int32_t col = n0 + wn * 64 + j * 32 + col_l;
+                if (col >= N) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int32_t rr = mrow + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
+                    if (rr < cnt)
+                        h[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 2][v]);
+                }
+            }
+    } else {
+        bf16_t* o = (bf16_t*)a.o;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int32_t col = n0 + wn * 128 + j * 32 + col_l;
+                if (col >= N) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int32_t rr = mrow + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
+                    if (rr < cnt) o[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[i][j][v]);
+                }
+            }
+    }
 }
 
 template <int BM, bool SWIGLU>
@@ -512,37 +307,195 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
         mfma_step(1, next, kt + 1, 0, 0);
     }
 
-    const int col_l = lane & 31, rgrp = (lane >> 5) * 4;
-    if (SWIGLU) {
-        bf16_t* h = (bf16_t*)a.h;
+    tile_epilogue<MT, SWIGLU>(a, acc, r0, cnt, m0 + wm * WM, n0, N, wn, lane);
+}
+
+
+// ---------------------------------------------------------------------------------------------
+// 4-bit weights (affine, groups of 64 along the reduction axis), tiles of 128 rows.  Same tile
+// shape, activation ring and tile list as gemm_dma; the packed codes are four times smaller than
+// bf16 rows, so they skip LDS: each lane loads the codes it multiplies straight into registers,
+// two stages ahead, with its row's scale and offset for the stage (one 64-k stage is one
+// quantisation group), and forms bf16(s*q + b) one k16 step before the MFMAs that consume it.
+// The dequantisation runs on the vector ALU beside the matrix cores; to keep it at one pass per
+// weight the four waves split the tile by columns (1 x 4): wave w owns all 128 rows and, for
+// GEMM-1, the gate and up rows of output columns [32 w, 32 w + 32), for GEMM-2 the 64 columns
+// [64 w, 64 w + 64).  Within a stage the k chunks are taken in the order 4h + s (lane half h,
+// step s) for both operands, so a lane's codes for the whole stage are one 16-byte load.
+// Per wave and stage the vector-memory issue order is: codes/scales of stage kt+2, then the
+// activation DMA of stage kt+NQ (A_DMA loads).  At the barrier before the last step of stage
+// kt everything but the newest A_DMA operations must have landed: that covers the activations
+// and the codes of stage kt+1.
+// ---------------------------------------------------------------------------------------------
+namespace q4t {
+constexpr int BM = 128;
+constexpr int NQ = 3;  // activation ring depth
+constexpr int ring_bytes() { return NQ * BM * dma::ROWB; }
+}  // namespace q4t
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
+    using namespace dma;
+    using q4t::NQ;
+    constexpr int BM = q4t::BM;
+    constexpr int MT = BM / 32;                // 32-row blocks per wave (all rows of the tile)
+    constexpr int A_BYTES = BM * ROWB;
+    constexpr int A_DMA = A_BYTES / 1024 / 4;  // DMA instructions per wave per stage
+    static_assert(q4t::ring_bytes() <= LDS_MAX, "ring exceeds LDS");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const GroupedArgs& a = ta.a;
+    int32_t tile, ct;
+    if (!map_tile(ta, tile, ct)) return;
+    const int32_t g = ta.tile_info[2 * tile], m0 = ta.tile_info[2 * tile + 1];
+    if (g < ta.g0 || g >= ta.g1 || g >= a.E) return;  // routed groups only (the shared expert is bf16)
+    const int32_t r0 = a.offsets[g];
+    const int32_t cnt = a.offsets[g + 1] - r0;
+    const int32_t N = SWIGLU ? a.I : a.H;
+    const int32_t KD = SWIGLU ? a.H : a.I;
+    constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
+    const int32_t n0 = ct * OUT_COLS;
+    if (n0 >= N) return;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5;
+
+    const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
+    uint32_t a_off[A_DMA];
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int32_t col = n0 + wn * 64 + j * 32 + col_l;
-                if (col >= N) continue;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int32_t rr = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                    if (rr < cnt)
-                        h[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 2][v]);
-                }
-            }
-    } else {
-        bf16_t* o = (bf16_t*)a.o;
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int32_t col = n0 + wn * 128 + j * 32 + col_l;
-                if (col >= N) continue;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int32_t rr = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                    if (rr < cnt) o[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[i][j][v]);
-                }
-            }
+    for (int j = 0; j < A_DMA; ++j) {
+        const int r = (wave * A_DMA + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        int32_t rr = m0 + r;
+        rr = rr < cnt ? rr : cnt - 1;  // rows past the group are computed, never stored
+        const int32_t row = r0 + rr;
+        if (SWIGLU) {
+            const int32_t tok = a.sorted_slot[row] / a.K;
+            a_off[j] = (uint32_t)tok * (uint32_t)a.H + c * 8;
+        } else {
+            a_off[j] = (uint32_t)row * (uint32_t)a.ldh + c * 8;
+        }
     }
+    // output column of B block j for this lane: GEMM-1 gate (j = 0) and up (j = 1) rows of
+    // column 32 w + lane % 32; GEMM-2 rows 64 w + 32 j + lane % 32.  The expert's matrices are
+    // uniform bases; per lane only 32-bit offsets within them are kept.
+    const int64_t eq = (int64_t)g * N * (KD / 8), es = (int64_t)g * N * (KD / 64);
+    const uint32_t* qb0 = (const uint32_t*)(SWIGLU ? a.wg : a.wd) + eq;
+    const uint32_t* qb1 = (const uint32_t*)(SWIGLU ? a.wu : a.wd) + eq;
+    const bf16_t* sb0 = (SWIGLU ? a.sg : a.sd) + es;
+    const bf16_t* sb1 = (SWIGLU ? a.su : a.sd) + es;
+    const bf16_t* bb0 = (SWIGLU ? a.bg : a.bd) + es;
+    const bf16_t* bb1 = (SWIGLU ? a.bu : a.bd) + es;
+    int32_t ncol[2];
+    uint32_t qoff[2], soff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        ncol[j] = n0 + (SWIGLU ? wave * 32 : wave * 64 + j * 32) + (lane & 31);
+        const int32_t n = ncol[j] < N ? ncol[j] : N - 1;  // columns past N are computed, never stored
+        qoff[j] = (uint32_t)n * (uint32_t)(KD / 8) + half * 4;
+        soff[j] = (uint32_t)n * (uint32_t)(KD / 64);
+    }
+    struct BStage {
+        u32x4 q[2];
+        bf16_t s[2], b[2];
+    };
+    auto load_b = [&](int kt, BStage& st) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            st.q[j] = *(const u32x4*)((j ? qb1 : qb0) + qoff[j] + kt * 8);
+            st.s[j] = (j ? sb1 : sb0)[soff[j] + kt];
+            st.b[j] = (j ? bb1 : bb0)[soff[j] + kt];
+        }
+    };
+    auto issue_a = [&](int kt) {
+        char* st = smem + (kt % NQ) * A_BYTES;
+        const int32_t k0 = kt * BKD;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)(a_base + a_off[j] + k0),
+                                             DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024), 16, 0, 0);
+    };
+
+    f32x16 acc[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = f32x16{};
+
+    const int nk = KD / BKD;  // >= 1
+    bf16x8 fa[2][MT], fb[2][2];
+    // operands of step s of stage kt: activations from LDS, weights dequantised from registers
+    auto frags = [&](int kt, int s, int buf, const BStage& bs) {
+        const char* st = smem + (kt % NQ) * A_BYTES;
+        const int c = 4 * half + s;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) fa[buf][i] = as_bf16x8(*(const u32x4*)(st + off(i * 32 + (lane & 31), c)));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            fb[buf][j] = as_bf16x8(dequant8(bs.q[j][s], bf16_to_f32(bs.s[j]), bf16_to_f32(bs.b[j])));
+    };
+    auto mfma_step = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+    };
+    // one stage; `cur` holds its codes, `nxt` those of stage kt+1 (landed by the barrier)
+    auto stage = [&](int kt, BStage& cur, const BStage& nxt) {
+        frags(kt, 1, 1, cur);
+        mfma_step(0);
+        frags(kt, 2, 0, cur);
+        mfma_step(1);
+        frags(kt, 3, 1, cur);
+        mfma_step(0);
+        const bool next = kt + 1 < nk;
+        if (next) {
+            // A(kt+2) (issued last, during stage kt-1) may still fly; all older loads must land
+            if (kt >= 1 && kt + 2 < nk) wait_vm_barrier<A_DMA>();
+            else wait_vm_barrier<0>();
+            if (kt + 2 < nk) load_b(kt + 2, cur);  // cur's codes are all dequantised
+            if (kt + NQ < nk) issue_a(kt + NQ);    // the slot of stage kt is fully read
+            frags(kt + 1, 0, 0, nxt);
+        }
+        mfma_step(1);
+    };
+
+    BStage b0, b1;
+    const int pro = min(nk, NQ);
+    for (int j = 0; j < pro; ++j) issue_a(j);
+    load_b(0, b0);
+    if (nk > 1) load_b(1, b1);
+    wait_vm_barrier<0>();
+    frags(0, 0, 0, b0);
+    for (int kt = 0; kt < nk; kt += 2) {  // two code sets, alternating by stage parity
+        stage(kt, b0, b1);
+        if (kt + 1 < nk) stage(kt + 1, b1, b0);
+    }
+
+    // the accumulators of the last MFMAs are read right away: give the MFMA-to-VALU wait states
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (i | j) asm volatile("" : "+a"(acc[i][j]));
+
+    const int rgrp = (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
+            const int32_t col = ncol[j];
+            if (col >= N) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int32_t rr = m0 + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
+                if (rr >= cnt) continue;
+                if (SWIGLU)
+                    ((bf16_t*)a.h)[(int64_t)(r0 + rr) * a.ldh + col] =
+                        f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+                else
+                    ((bf16_t*)a.o)[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[i][j][v]);
+            }
+        }
 }
 
 // Tile list: every group in [0, E] (E = shared expert) with more than `min_rows` rows gets
@@ -595,13 +548,14 @@ hipError_t launch_dma_t(const TileArgs& ta, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BM, bool SW, int WF>
-hipError_t launch_tiled_t(const TileArgs& ta, hipStream_t s) {
-    const size_t lds = 2 * (size_t)(BM + NB) * 128;
-    const unsigned grid = (unsigned)(((ta.nwg + 7) / 8) * 8);  // the XCD remap needs a multiple of 8
-    hipLaunchKernelGGL((gemm_tiled<BM, SW, WF>), dim3(grid), dim3(THREADS), lds, s, ta);
+template <bool SW>
+hipError_t launch_dma_q4_t(const TileArgs& ta, hipStream_t s) {
+    const size_t lds = (size_t)q4t::ring_bytes();
+    const unsigned grid = (unsigned)(((ta.nwg + 7) / 8) * 8);
+    hipLaunchKernelGGL((gemm_dma_q4<SW>), dim3(grid), dim3(THREADS), lds, s, ta);
     return hipGetLastError();
 }
+
 
 }  // namespace
 
@@ -612,20 +566,18 @@ int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM) {
 
 // largest dynamic LDS any tiled kernel of this tile height uses
 int32_t tiled_lds_bytes(int32_t BM) {
-    const int32_t reg_staged = 2 * (BM + NB) * 128, dma_ring = dma::ring_bytes(BM);
-    return reg_staged > dma_ring ? reg_staged : dma_ring;
+    const int32_t dma_ring = dma::ring_bytes(BM), q4_ring = q4t::ring_bytes();
+    return BM == q4t::BM && q4_ring > dma_ring ? q4_ring : dma_ring;
 }
 
 hipError_t configure_tiled_kernels() {
     // allow the large dynamic LDS allocations (up to 128 KB) of the tiled kernels
     const void* ks[] = {
-        (const void*)gemm_dma<256, true>,          (const void*)gemm_dma<256, false>,
-        (const void*)gemm_tiled<256, true, WF_Q4>, (const void*)gemm_tiled<256, false, WF_Q4>,
-        (const void*)gemm_dma<128, true>,          (const void*)gemm_dma<128, false>,
-        (const void*)gemm_tiled<128, true, WF_Q4>, (const void*)gemm_tiled<128, false, WF_Q4>,
+        (const void*)gemm_dma<256, true>, (const void*)gemm_dma<256, false>, (const void*)gemm_dma<128, true>,
+        (const void*)gemm_dma<128, false>, (const void*)gemm_dma_q4<true>,   (const void*)gemm_dma_q4<false>,
     };
-    const int bms[] = {256, 256, 256, 256, 128, 128, 128, 128};
-    for (int i = 0; i < 8; ++i) {
+    const int bms[] = {256, 256, 128, 128, 128, 128};
+    for (int i = 0; i < 6; ++i) {
         hipError_t e = hipFuncSetAttribute(ks[i], hipFuncAttributeMaxDynamicSharedMemorySize, tiled_lds_bytes(bms[i]));
         if (e != hipSuccess) return e;
     }
@@ -657,8 +609,9 @@ hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32
         if (BM == 256) return gemm1 ? launch_dma_t<256, true>(ta, s) : launch_dma_t<256, false>(ta, s);
         return gemm1 ? launch_dma_t<128, true>(ta, s) : launch_dma_t<128, false>(ta, s);
     }
-    if (BM == 256) return gemm1 ? launch_tiled_t<256, true, WF_Q4>(ta, s) : launch_tiled_t<256, false, WF_Q4>(ta, s);
-    return gemm1 ? launch_tiled_t<128, true, WF_Q4>(ta, s) : launch_tiled_t<128, false, WF_Q4>(ta, s);
+    // 4-bit layers always use tiles of 128 rows (plan_tiles)
+    if (BM != 128) return hipErrorInvalidValue;
+    return gemm1 ? launch_dma_q4_t<true>(ta, s) : launch_dma_q4_t<false>(ta, s);
 }
 
 }  // namespace dsmoe

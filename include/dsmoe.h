@@ -161,15 +161,11 @@ int moe_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* 
  *   y[t] = shared(x[t]) + sum_{j<K} scores[t,j] * expert_{inds[t,j]}(x[t])
  *   expert(x) = W_down (silu(W_gate x) * (W_up x))   (SwiGLU; the gate projection is the one
  *                                                      that goes through silu)
- * Steps, in `stream` order: router logits (as moe_router_logits) -> gate (as
- * moe_route_deepseek) -> dispatch (as moe_dispatch) -> grouped gate/up GEMM with SwiGLU in the
- * epilogue -> grouped down GEMM -> combine.  For bf16 and 4-bit layers with T > 64, the
- * expert groups of at most 64 rows are computed by weight-streaming kernels on a second,
- * library-owned stream (default priority; one per device and caller stream, created on the
- * first such call and kept until the process ends) that forks from `stream` after the dispatch
- * and joins it before the combine, so that they overlap the MFMA-tiled GEMMs of the larger
- * groups.  Work queued on `stream` after the call still sees the whole result.  Calls on one
- * stream must not be issued from several host threads at once.  The combine adds, per token and output element, the shared expert's
+ * Steps, all on `stream`: router logits (as moe_router_logits) -> gate (as moe_route_deepseek)
+ * -> dispatch (as moe_dispatch) -> grouped gate/up GEMM with SwiGLU in the epilogue -> grouped
+ * down GEMM -> combine.  For bf16 and 4-bit layers with T > 64, each grouped GEMM is two
+ * kernels: weight streaming for the expert groups of at most 64 rows, MFMA tiles for the
+ * larger groups and the shared expert.  The combine adds, per token and output element, the shared expert's
  * output and then the K weighted expert outputs in j order in fp32, with no atomics.
  * Precision: bf16 layers run bf16 MFMA with fp32 accumulation; the SwiGLU intermediate and the
  * per-expert outputs are rounded to bf16; y is rounded to act_dtype (nearest-even).  4-bit
@@ -201,9 +197,9 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
  *   scatter), MOE_STAGE_GEMM1 (gate/up + SwiGLU), MOE_STAGE_GEMM2 (down), MOE_STAGE_COMBINE.
  * While a hook is set, every moe_forward call records events[2*i] on its stream right before
  * the first kernel of `stage` and events[2*i + 1] right after the stage's last kernel, with
- * i = (moe_forward calls since the hook was set) mod n_pairs.  When the streaming kernels run
- * on the side stream (see moe_forward), the GEMM1 and GEMM2 pairs bracket only the tiled
- * kernels on the caller's stream.  events are hipEvent_t handles
+ * i = (moe_forward calls since the hook was set) mod n_pairs.  When a grouped GEMM is split
+ * into streaming and tiled kernels (see moe_forward), the GEMM1 and GEMM2 pairs bracket the
+ * tiled kernels only.  events are hipEvent_t handles
  * owned by the caller (created with timing enabled) and must outlive the hook.  stage = -1 (or
  * n_pairs = 0) clears the hook.  The hook is process-wide and not thread-safe: set it only
  * while one thread drives moe_forward.  Errors: -1 for a stage out of range, n_pairs < 0, or
