@@ -28,6 +28,15 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE-layer tokens/sec (DeepSeek-V3 shape, bf16) + % HBM/MFMA peak"
 
+# HBM-side traffic of the dominant kernel, GB per launch: rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE passes over this script, each scaled by what the same counter reads for the plain
+# 256 MiB device copy that main() runs first (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  The summaries
+# are kept with the kernel traces; an entry goes back to None whenever its kernel changes.
+TRAFFIC_GB = {
+    "c3": 11.82,  # gemm_dma<256, true>: 5,623,600 KiB fetched, 292,503 KiB written per launch
+    "c2": 7.48,   # stream_gemm<bf16, gate/up>: 3,652,704 KiB fetched, 2,308 KiB written per launch
+}
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -231,14 +240,16 @@ def main():
         if decode:
             ach = gemm1_bytes(wl, res["n_hit"]) / (res["gemm1_ms"] / 1e3) / 1e9
             roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                    "traffic": None, "kernel": "gemm1_stream (gate/up + SwiGLU)"}
+                    "traffic": TRAFFIC_GB.get(wl.name), "traffic_unit": "GB per launch",
+                    "kernel": "stream_gemm<bf16, gate/up> (weight-streaming gate/up + SwiGLU)"}
             layer = layer_bytes(wl, res["n_hit"]) / (res["step_ms"] / 1e3) / 1e9
             roof["layer_achieved"] = layer
             roof["layer_frac"] = layer / PEAK_HBM_GBS
         else:
             ach = tiled_gemm1_flops(wl, res["counts"]) / (res["gemm1_ms"] / 1e3) / 1e12
             roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                    "frac": ach / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_GB.get(wl.name),
+                    "traffic_unit": "GB per launch",
                     "kernel": ("gemm_dma<256, true> (tiled gate/up + SwiGLU: groups above 64 rows and the "
                                "shared expert)") if wl.expert == "bf16" else
                               ("tiled gate/up + SwiGLU kernels: gemm_tiled<BM, true, q4> for the 4-bit routed "
