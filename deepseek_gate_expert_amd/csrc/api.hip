@@ -53,10 +53,13 @@ struct TilePlan {
 TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     TilePlan p{false, 128, 0};
     if (d->act_dtype != MOE_BF16 || d->T <= STREAM_MAX_ROWS) return p;
-    // the tiled kernels address activation rows with 32-bit element offsets
+    // the tiled kernels address activation and weight rows with 32-bit byte offsets
     const int64_t rows = d->T * d->route.top_k + d->T;
     const int64_t ldh = d->I > d->I_shared ? d->I : d->I_shared;
-    if (d->T * (int64_t)d->H >= ((int64_t)1 << 32) || rows * ldh >= ((int64_t)1 << 32)) return p;
+    const int64_t lim = (int64_t)1 << 31;  // elements of 2 bytes
+    if (d->T * (int64_t)d->H >= lim || rows * ldh >= lim || (int64_t)d->I * d->H >= lim ||
+        (int64_t)d->I_shared * d->H >= lim)
+        return p;
     p.on = true;
     const int64_t avg = d->T * d->route.top_k / d->E;
     p.BM = (allow256 && avg >= 192 && d->expert_dtype == MOE_BF16) ? 256 : 128;

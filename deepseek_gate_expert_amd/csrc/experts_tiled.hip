@@ -192,7 +192,8 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
     const int32_t n0 = ct * OUT_COLS;
     if (n0 >= N) return;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is uniform: keep it scalar so the DMA destinations (M0) are scalar too
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
 
     // ---- DMA sources: instruction j of this wave fills LDS rows [8 (wave*X + j), +8); lane i
@@ -208,9 +209,9 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
         const int32_t row = r0 + rr;
         if (SWIGLU) {
             const int32_t tok = row < a.TK ? a.sorted_slot[row] / a.K : row - a.TK;
-            a_off[j] = (uint32_t)tok * (uint32_t)a.H + c * 8;
+            a_off[j] = ((uint32_t)tok * (uint32_t)a.H + c * 8) * 2u;
         } else {
-            a_off[j] = (uint32_t)row * (uint32_t)a.ldh + c * 8;
+            a_off[j] = ((uint32_t)row * (uint32_t)a.ldh + c * 8) * 2u;
         }
     }
     const bf16_t *wb0, *wb1;
@@ -230,21 +231,24 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
         const int c = (lane & 7) ^ swz(br);
         int32_t n = n0 + (SWIGLU ? br % (NB / 2) : br);
         n = n < N ? n : N - 1;  // columns past N are computed, never stored
-        b_off[j] = (uint32_t)n * (uint32_t)KD + c * 8;
+        b_off[j] = ((uint32_t)n * (uint32_t)KD + c * 8) * 2u;
     }
     // a wave's B instruction j covers 8 rows, all gate or all up (NB/2 is a multiple of 8)
+    // DMA sources are a uniform base (advanced by the stage) plus a per-lane 32-bit byte offset,
+    // so no per-lane 64-bit address arithmetic is issued per instruction
     auto issue = [&](int kt) {
         char* st = smem + (kt % NST) * ST_BYTES;
         const int32_t k0 = kt * BKD;
+        const char* ab = (const char*)(a_base + k0);
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
-            __builtin_amdgcn_global_load_lds((const void*)(a_base + a_off[j] + k0),
+            __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[j]),
                                              DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < B_DMA; ++j) {
             const int br0 = (wave * B_DMA + j) * 8;
-            const bf16_t* wb = (SWIGLU && br0 >= NB / 2) ? wb1 : wb0;
-            __builtin_amdgcn_global_load_lds((const void*)(wb + b_off[j] + k0),
+            const char* wb = (const char*)(((SWIGLU && br0 >= NB / 2) ? wb1 : wb0) + k0);
+            __builtin_amdgcn_global_load_lds((const void*)(wb + b_off[j]),
                                              DSMOE_LDS_PTR(st + A_BYTES + (wave * B_DMA + j) * 1024), 16, 0, 0);
         }
     };
@@ -357,7 +361,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
     const int32_t n0 = ct * OUT_COLS;
     if (n0 >= N) return;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5;
 
     const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
     uint32_t a_off[A_DMA];
@@ -370,9 +374,9 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
         const int32_t row = r0 + rr;
         if (SWIGLU) {
             const int32_t tok = a.sorted_slot[row] / a.K;
-            a_off[j] = (uint32_t)tok * (uint32_t)a.H + c * 8;
+            a_off[j] = ((uint32_t)tok * (uint32_t)a.H + c * 8) * 2u;
         } else {
-            a_off[j] = (uint32_t)row * (uint32_t)a.ldh + c * 8;
+            a_off[j] = ((uint32_t)row * (uint32_t)a.ldh + c * 8) * 2u;
         }
     }
     // output column of B block j for this lane: GEMM-1 gate (j = 0) and up (j = 1) rows of
@@ -408,10 +412,10 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
     };
     auto issue_a = [&](int kt) {
         char* st = smem + (kt % NQ) * A_BYTES;
-        const int32_t k0 = kt * BKD;
+        const char* ab = (const char*)(a_base + kt * BKD);
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
-            __builtin_amdgcn_global_load_lds((const void*)(a_base + a_off[j] + k0),
+            __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[j]),
                                              DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024), 16, 0, 0);
     };
 
