@@ -53,7 +53,7 @@ class Layer(ctypes.Structure):
                 ("Is", ctypes.c_int32), ("act", ctypes.c_int32), ("expert", ctypes.c_int32),
                 ("route", RouteParams)] + [(n, ctypes.c_void_p) for n in (
                     "x", "router", "bias", "offset", "wg", "wu", "wd", "sg", "bg", "su", "bu", "sd", "bd",
-                    "swg", "swu", "swd")]
+                    "swg", "swu", "swd")] + [("route_kind", ctypes.c_int32), ("sgate", ctypes.c_void_p)]
 
 
 _lib = None
@@ -73,6 +73,8 @@ def _L():
         lib.oracle_router.argtypes = [p, p, i32, i64, i32, i32, p, p]
         lib.oracle_route.restype = ctypes.c_int
         lib.oracle_route.argtypes = [p, i64, i32, p, ctypes.POINTER(RouteParams), p, p]
+        lib.oracle_route_softmax.restype = ctypes.c_int
+        lib.oracle_route_softmax.argtypes = [p, i64, i32, i32, p, p]
         lib.oracle_swiglu.restype = None
         lib.oracle_swiglu.argtypes = [p, i32, i32, i32] + [p] * 9 + [p]
         lib.oracle_forward.restype = ctypes.c_int
@@ -135,6 +137,18 @@ def route(logits: np.ndarray, bias: np.ndarray, p: RouteParams):
     return rc, inds, scores
 
 
+def route_softmax(logits: np.ndarray, top_k: int):
+    """Softmax gate; returns (rc, inds, scores) like `route`."""
+    logits = np.ascontiguousarray(logits, np.float32)
+    E = logits.shape[-1]
+    T = logits.size // E if E else 0
+    K = max(int(top_k), 1)
+    inds = np.full((T, K), -7, np.int32)
+    scores = np.full((T, K), -7.0, np.float32)
+    rc = _L().oracle_route_softmax(_p(logits), T, E, int(top_k), _p(inds), _p(scores))
+    return rc, inds, scores
+
+
 def swiglu(x: np.ndarray, wg, wu, wd, dtype: str, q4: Optional[dict] = None) -> np.ndarray:
     """One expert on one row: W_down(silu(W_gate x) * (W_up x)), fp64."""
     x = np.ascontiguousarray(x, np.float64)
@@ -150,9 +164,11 @@ def swiglu(x: np.ndarray, wg, wu, wd, dtype: str, q4: Optional[dict] = None) -> 
 
 def forward(x, router_w, bias, experts: dict, shared: Optional[dict], *, T, H, E, I, Is, K, G, TG, norm,
             rsf, act: str, expert: str, offset: Optional[np.ndarray] = None,
-            rows: Optional[Sequence[int]] = None):
+            rows: Optional[Sequence[int]] = None, route_kind: str = "deepseek",
+            shared_gate: Optional[np.ndarray] = None):
     """Whole layer; returns (y fp64 [n,H], inds [n,K], scores [n,K], logits [n,E]) for the
-    tokens `rows` (all tokens when None)."""
+    tokens `rows` (all tokens when None).  route_kind: "deepseek" (sigmoid gate with bias and
+    groups) or "softmax"; shared_gate: optional [H] vector gating the shared expert."""
     keep = []
 
     def c(a, dt=None):
@@ -175,6 +191,8 @@ def forward(x, router_w, bias, experts: dict, shared: Optional[dict], *, T, H, E
         L.sd, L.bd = c(experts["s_down"]), c(experts["b_down"])
     if shared is not None and Is > 0:
         L.swg, L.swu, L.swd = c(shared["gate"]), c(shared["up"]), c(shared["down"])
+    L.route_kind = {"deepseek": 0, "softmax": 1}[route_kind]
+    L.sgate = c(shared_gate)
     rr = None if rows is None else np.ascontiguousarray(np.asarray(rows, np.int64))
     n = T if rr is None else len(rr)
     y = np.empty((n, H), np.float64)
@@ -187,10 +205,11 @@ def forward(x, router_w, bias, experts: dict, shared: Optional[dict], *, T, H, E
     return y, inds, scores, logits
 
 
-def forward_workload(w, x, router_w, bias, experts, shared, offset=None, rows=None):
+def forward_workload(w, x, router_w, bias, experts, shared, offset=None, rows=None, shared_gate=None):
     """`forward` with the shape/route parameters taken from a synth.Workload."""
     return forward(x, router_w, bias, experts, shared, T=w.T, H=w.H, E=w.E, I=w.I, Is=w.Is, K=w.K, G=w.G,
-                   TG=w.TG, norm=w.norm, rsf=w.rsf, act=w.act, expert=w.expert, offset=offset, rows=rows)
+                   TG=w.TG, norm=w.norm, rsf=w.rsf, act=w.act, expert=w.expert, offset=offset, rows=rows,
+                   route_kind=getattr(w, "route", "deepseek"), shared_gate=shared_gate)
 
 
 def dispatch(inds: np.ndarray, E: int):

@@ -99,6 +99,8 @@ typedef struct {
     int32_t i;
 } vi_t;
 
+#define MAX_TOPK_ORACLE 1024
+
 /* Total order used for every selection: larger value first; equal values (so -0 == +0)
  * by smaller index; NaN after every number. */
 static int vi_cmp(const void* pa, const void* pb) {
@@ -193,6 +195,49 @@ int oracle_route(const float* logits, int64_t T, int32_t E, const float* bias, c
     return 0;
 }
 
+/* Softmax gate, the sibling route of [PR123] ("API": it shares the DeepSeek route's output
+ * contract, inds and scores [.., K]; second review, S2: unlike the DeepSeek route's top_k > 1
+ * guard, it normalises its weights in every case).  The pages print nothing more; the
+ * reading taken, one row:
+ *   m = max_e logit_e;  ex_e = oracle_exp(logit_e - m)  (fp32)
+ *   S = ((ex_0 + ex_1) + ex_2) + ...                       (fp32, index order)
+ *   inds = top_k of ex (ties -> lower index; order: ex desc, index asc)
+ *   p_j = ex[inds_j] / S;  W = ((p_0 + p_1) + ...);  scores_j = p_j / W
+ * No bias, no groups, no scaling factor.  Ranking by ex (rather than by ex / S) keeps the
+ * selection independent of how S is summed. */
+static void route_softmax_row(const float* lg, int32_t E, int32_t K, vi_t* b, int32_t* inds, float* scores) {
+    float m = lg[0];
+    for (int32_t e = 1; e < E; ++e) m = lg[e] > m ? lg[e] : m;
+    float S = 0.0f;
+    for (int32_t e = 0; e < E; ++e) {
+        b[e].v = oracle_exp(lg[e] - m);
+        b[e].i = e;
+        S = e == 0 ? b[e].v : S + b[e].v;
+    }
+    float ex[MAX_TOPK_ORACLE];
+    qsort(b, (size_t)E, sizeof(vi_t), vi_cmp);
+    for (int32_t j = 0; j < K; ++j) {
+        inds[j] = b[j].i;
+        ex[j] = b[j].v / S;
+    }
+    float W = 0.0f;
+    for (int32_t j = 0; j < K; ++j) W = j == 0 ? ex[0] : W + ex[j];
+    for (int32_t j = 0; j < K; ++j) scores[j] = ex[j] / W;
+}
+
+int oracle_route_softmax(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* inds, float* scores) {
+    if (!logits || !inds || !scores || T < 0 || E < 1 || top_k < 1 || top_k > E || top_k > MAX_TOPK_ORACLE)
+        return -1;
+#pragma omp parallel
+    {
+        vi_t* b = (vi_t*)malloc(sizeof(vi_t) * (size_t)E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) route_softmax_row(logits + t * E, E, top_k, b, inds + t * top_k, scores + t * top_k);
+        free(b);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------------------
  * experts
  * ------------------------------------------------------------------------------------ */
@@ -252,7 +297,9 @@ static const uint16_t* expert_sb(const uint16_t* base, int64_t e, int32_t out, i
  */
 int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, double* y, int32_t* inds,
                    float* scores, float* logits) {
-    if (!L || !y || !L->x || !L->router || !L->bias || !L->wg || !L->wu || !L->wd) return -1;
+    if (!L || !y || !L->x || !L->router || !L->wg || !L->wu || !L->wd) return -1;
+    if (L->route_kind != 0 && L->route_kind != 1) return -1;
+    if (L->route_kind == 0 && !L->bias) return -1;
     const int32_t H = L->H, E = L->E, I = L->I, Is = L->Is, K = L->route.top_k;
     if (L->T < 0 || n_rows < 0 || H < 1 || I < 1 || Is < 0 || K < 1 || K > E) return -1;
     if (L->act != 0 && L->act != 1) return -1;
@@ -277,7 +324,16 @@ int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, d
     int32_t* id = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_rows * K + 1);
     float* sc = (float*)malloc(sizeof(float) * (size_t)n_rows * K + 1);
     oracle_router(xs, L->router, L->act, n_rows, H, E, L->offset, lg);
-    if (oracle_route(lg, n_rows, E, L->bias, &L->route, id, sc) != 0) {
+    const int rrc = L->route_kind == 0 ? oracle_route(lg, n_rows, E, L->bias, &L->route, id, sc)
+                                       : oracle_route_softmax(lg, n_rows, E, K, id, sc);
+    /* shared-expert gate: g = sigmoid(x . w_sgate), the dot product in the router's order */
+    float* sgl = NULL;
+    if (Is > 0 && L->sgate) {
+        sgl = (float*)malloc(sizeof(float) * (size_t)n_rows + 1);
+        oracle_router(xs, L->sgate, L->act, n_rows, H, 1, NULL, sgl);
+    }
+    if (rrc != 0) {
+        free(sgl);
         free(xs);
         free(lg);
         free(id);
@@ -311,10 +367,12 @@ int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, d
         }
         free(xd);
     }
-    /* combine: shared output (weight 1) plus the weighted routed outputs, j ascending */
+    /* combine: shared output (weight 1, or its sigmoid gate) plus the weighted routed
+     * outputs, j ascending */
     for (int64_t r = 0; r < n_rows; ++r) {
+        const double gs = sgl ? (double)oracle_sigmoid(sgl[r]) : 1.0;
         for (int32_t m = 0; m < H; ++m) {
-            double acc = Is > 0 ? o[((size_t)r * KS + K) * H + m] : 0.0;
+            double acc = Is > 0 ? gs * o[((size_t)r * KS + K) * H + m] : 0.0;
             for (int32_t j = 0; j < K; ++j) acc += (double)sc[r * K + j] * o[((size_t)r * KS + j) * H + m];
             y[r * (int64_t)H + m] = acc;
         }
@@ -327,6 +385,7 @@ int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, d
     free(id);
     free(sc);
     free(o);
+    free(sgl);
     return 0;
 }
 

@@ -56,6 +56,8 @@ typedef struct oracle_layer {
     const void* swg;      /* [Is,H] act */
     const void* swu;      /* [Is,H] act */
     const void* swd;      /* [H,Is] act */
+    int32_t route_kind;   /* 0: DeepSeek sigmoid gate (oracle_route); 1: softmax gate (oracle_route_softmax) */
+    const void* sgate;    /* NULL, or [H] act: the shared expert's output is scaled by sigmoid(x . sgate) */
 } oracle_layer;
 
 /* exp by Cody-Waite range reduction + degree-7 Taylor polynomial, fp32 (see oracle.c) */
@@ -71,6 +73,9 @@ void oracle_router(const void* x, const void* w, int32_t dtype, int64_t T, int32
 int oracle_route(const float* logits, int64_t T, int32_t E, const float* bias, const oracle_route_params* p,
                  int32_t* inds, float* scores);
 
+/* Softmax gate over T rows (see oracle.c for the reading taken).  Returns 0, or -1 on
+ * invalid arguments (outputs untouched). */
+int oracle_route_softmax(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* inds, float* scores);
 /* SwiGLU expert on one fp64 input row: out[H] = W_down (silu(W_gate x) * (W_up x)).
  * w* point at ONE expert's matrices in `dtype`; s*, b* are its q4 scale/offset (or NULL). */
 void oracle_swiglu(const double* x, int32_t H, int32_t I, int32_t dtype, const void* wg, const void* wu,

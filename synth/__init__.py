@@ -32,7 +32,7 @@ _SO = os.path.join(_HERE, "libsynth.so")
 
 # tensor ids of the counter-based generator
 TID_X, TID_ROUTER, TID_BIAS, TID_WG, TID_WU, TID_WD = 1, 2, 3, 4, 5, 6
-TID_SWG, TID_SWU, TID_SWD, TID_ZIPF, TID_PLANT = 7, 8, 9, 10, 11
+TID_SWG, TID_SWU, TID_SWD, TID_ZIPF, TID_PLANT, TID_SGATE = 7, 8, 9, 10, 11, 12
 
 
 def build(force: bool = False) -> str:
@@ -146,6 +146,8 @@ class Workload:
     zipf_s: float = 0.0      # >0: per-expert logit offset -s*ln(1+perm(e))
     planted: int = 0         # rows realised so that the max expert's group loses on top-2 sum
     note: str = ""
+    route: str = "deepseek"  # gate: "deepseek" (sigmoid, bias, groups) or "softmax"
+    shared_gate: bool = False  # shared expert output scaled by sigmoid(x . w_sgate)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -264,6 +266,13 @@ def gen_expert_weights(w: Workload, e0: int = 0, e1: Optional[int] = None) -> di
         else:
             out[nm] = normal_f32(w.wseed, tid, n * o * i, std, start=start).reshape(n, o, i)
     return out
+
+
+def gen_shared_gate(w: Workload) -> Optional[np.ndarray]:
+    """[H] gate vector of the shared expert, N(0, 1/sqrt(H)) in the activation dtype, or None."""
+    if not w.shared_gate or w.Is <= 0:
+        return None
+    return _act_normal(w, TID_SGATE, w.H, 1.0 / math.sqrt(w.H), w.wseed)
 
 
 def gen_shared(w: Workload) -> Optional[dict]:
