@@ -24,8 +24,9 @@ LIB_PATH = os.path.join(_HERE, "libdsmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_HIP, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_Q4G64 = 0, 1, 2
 MOE_MAX_EXPERTS, MOE_MAX_TOP_K = 1024, 64
+MOE_ROUTE_DEEPSEEK, MOE_ROUTE_SOFTMAX = 0, 1
 MOE_STAGE_ROUTER, MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = range(6)
-EXPORTS = ("moe_router_logits", "moe_route_deepseek", "moe_dispatch_workspace_size", "moe_dispatch",
+EXPORTS = ("moe_router_logits", "moe_route_deepseek", "moe_route_softmax", "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_forward_workspace_size", "moe_forward", "moe_set_stage_events", "moe_strerror")
 
 
@@ -37,7 +38,7 @@ class RouteParams(ctypes.Structure):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("I_shared", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
-                ("route", RouteParams)]
+                ("route", RouteParams), ("route_kind", ctypes.c_int32)]
 
 
 class ExpertWeights(ctypes.Structure):
@@ -46,7 +47,7 @@ class ExpertWeights(ctypes.Structure):
 
 
 class SharedWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_up", "w_down")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_up", "w_down", "w_sgate")]
 
 
 _lib = None
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.moe_router_logits.argtypes = [p, p, i32, i64, i32, i32, p, p, p]
         lib.moe_route_deepseek.restype = ctypes.c_int
         lib.moe_route_deepseek.argtypes = [p, i64, i32, p, i64, ctypes.POINTER(RouteParams), p, p, p]
+        lib.moe_route_softmax.restype = ctypes.c_int
+        lib.moe_route_softmax.argtypes = [p, i64, i32, i32, p, p, p]
         lib.moe_dispatch_workspace_size.restype = sz
         lib.moe_dispatch_workspace_size.argtypes = [i64, i32, i32]
         lib.moe_dispatch.restype = ctypes.c_int
@@ -169,6 +172,24 @@ def moe_route_deepseek(logits, bias, inds, scores, top_k, n_group=1, topk_group=
                                              _ptr(inds), _ptr(scores), _stream(stream))
 
 
+def moe_route_softmax(logits, inds, scores, top_k, stream=None) -> int:
+    """Softmax gate on logits [..., E] (leading dims flatten to rows).  inds (int32) and scores
+    (fp32) are [..., top_k] and are written only on success."""
+    import torch
+    if logits.dim() < 1 or logits.dtype != torch.float32:
+        return MOE_ERR_INVALID
+    if inds.dtype != torch.int32 or scores.dtype != torch.float32:
+        return MOE_ERR_INVALID
+    if not _same_device(logits, inds, scores) or not _contig(logits, inds, scores):
+        return MOE_ERR_INVALID
+    E = logits.shape[-1]
+    T = logits.numel() // E if E > 0 else 0
+    if inds.numel() != T * max(int(top_k), 0) or scores.numel() != inds.numel():
+        return MOE_ERR_INVALID
+    return load_library().moe_route_softmax(_ptr(logits), T, E, int(top_k), _ptr(inds), _ptr(scores),
+                                            _stream(stream))
+
+
 def moe_dispatch_workspace_size(T: int, K: int, E: int) -> int:
     return int(load_library().moe_dispatch_workspace_size(T, K, E))
 
@@ -190,9 +211,10 @@ def moe_dispatch(inds, E, counts, offsets, sorted_slot, slot_row, workspace, str
 
 
 def layer_desc(T, H, E, I, I_shared, act_dtype, expert_dtype, top_k, n_group=1, topk_group=1, norm_topk_prob=True,
-               routed_scaling_factor=1.0) -> LayerDesc:
+               routed_scaling_factor=1.0, route_kind=MOE_ROUTE_DEEPSEEK) -> LayerDesc:
     return LayerDesc(int(T), int(H), int(E), int(I), int(I_shared), int(act_dtype), int(expert_dtype),
-                     route_params(top_k, n_group, topk_group, norm_topk_prob, routed_scaling_factor))
+                     route_params(top_k, n_group, topk_group, norm_topk_prob, routed_scaling_factor),
+                     int(route_kind))
 
 
 def moe_forward_workspace_size(desc: LayerDesc) -> int:
@@ -203,17 +225,18 @@ def moe_forward(desc: LayerDesc, x, router_w, bias, experts: dict, shared: Optio
                 inds_out=None, scores_out=None, workspace=None, stream=None) -> int:
     """Whole MoE layer forward (see dsmoe.h).  experts: dict with 'gate', 'up', 'down' (and for
     4-bit weights 's_gate', 'b_gate', 's_up', 'b_up', 's_down', 'b_down'); shared: dict with
-    'gate', 'up', 'down' or None."""
+    'gate', 'up', 'down' (and optionally 'sgate', the [H] gate vector) or None.  bias may be
+    None with the softmax gate."""
     import torch
     if not _contig(x, router_w, bias, y, logit_offset, inds_out, scores_out, workspace):
         return MOE_ERR_INVALID
-    if bias.dim() != 1 or bias.dtype != torch.float32:
+    if bias is not None and (bias.dim() != 1 or bias.dtype != torch.float32):
         return MOE_ERR_INVALID
     ew = ExpertWeights(*[_ptr(experts.get(k)) for k in
                          ("gate", "up", "down", "s_gate", "b_gate", "s_up", "b_up", "s_down", "b_down")])
     sw = None
     if shared is not None:
-        sw = SharedWeights(_ptr(shared["gate"]), _ptr(shared["up"]), _ptr(shared["down"]))
+        sw = SharedWeights(_ptr(shared["gate"]), _ptr(shared["up"]), _ptr(shared["down"]), _ptr(shared.get("sgate")))
     tensors = [x, router_w, bias, y, logit_offset, inds_out, scores_out, workspace] + \
         [v for v in experts.values()] + ([] if shared is None else list(shared.values()))
     if not _same_device(*tensors):

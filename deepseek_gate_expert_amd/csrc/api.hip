@@ -68,7 +68,7 @@ TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
 }
 
 struct FwdLayout {
-    size_t logits, inds, scores, blk, counts, offsets, sorted_slot, slot_row, tiles, h, o, total;
+    size_t logits, sgl, inds, scores, blk, counts, offsets, sorted_slot, slot_row, tiles, h, o, total;
 };
 
 FwdLayout fwd_layout(const moe_layer_desc* d) {
@@ -81,6 +81,8 @@ FwdLayout fwd_layout(const moe_layer_desc* d) {
     size_t off = 0;
     L.logits = off;
     off += up(T * E * 4);
+    L.sgl = off;  // shared-expert gate logits
+    off += up(T * 4);
     L.inds = off;
     off += up(TK * 4);
     L.scores = off;
@@ -111,7 +113,15 @@ int check_desc(const moe_layer_desc* d) {
     const int32_t a = d->act_dtype, w = d->expert_dtype;
     const bool combo = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_Q4G64));
     if (!combo) return MOE_ERR_INVALID;
-    int rc = check_route_params(d->E, &d->route);
+    if (d->route_kind != MOE_ROUTE_DEEPSEEK && d->route_kind != MOE_ROUTE_SOFTMAX) return MOE_ERR_INVALID;
+    int rc = MOE_OK;
+    if (d->route_kind == MOE_ROUTE_DEEPSEEK) {
+        rc = check_route_params(d->E, &d->route);
+    } else if (d->route.top_k < 1 || d->route.top_k > d->E) {
+        rc = MOE_ERR_INVALID;
+    } else if (d->E > MOE_MAX_EXPERTS || d->route.top_k > MOE_MAX_TOP_K) {
+        rc = MOE_ERR_UNSUPPORTED;
+    }
     if (rc != MOE_OK) return rc;
     if ((int64_t)d->T * (d->route.top_k + 1) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (a == MOE_BF16 && (d->H % 64 || d->I % 64 || d->I_shared % 64)) return MOE_ERR_UNSUPPORTED;
@@ -192,6 +202,16 @@ int moe_router_logits(const void* x, const void* router_w, int32_t act_dtype, in
     return hip_rc(launch_router(x, router_w, act_dtype, T, H, E, logit_offset, logits, (hipStream_t)stream));
 }
 
+int moe_route_softmax(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* inds, float* scores,
+                      void* stream) {
+    if (T < 0 || E < 1 || top_k < 1 || top_k > E) return MOE_ERR_INVALID;
+    const bool empty = T == 0;
+    if (!ptr_ok(logits, empty) || !ptr_ok(inds, empty) || !ptr_ok(scores, empty)) return MOE_ERR_INVALID;
+    if (E > MOE_MAX_EXPERTS || top_k > MOE_MAX_TOP_K) return MOE_ERR_UNSUPPORTED;
+    if (empty) return MOE_OK;
+    return hip_rc(launch_route_softmax(logits, T, E, top_k, inds, scores, (hipStream_t)stream));
+}
+
 int moe_route_deepseek(const float* logits, int64_t T, int32_t E, const float* bias, int64_t bias_len,
                        const moe_route_params* p, int32_t* inds, float* scores, void* stream) {
     if (T < 0) return MOE_ERR_INVALID;
@@ -236,7 +256,8 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     int rc = check_desc(d);
     if (rc != MOE_OK) return rc;
     const bool empty = d->T == 0;
-    if (!ptr_ok(x, empty) || !ptr_ok(router_w, false) || !ptr_ok(bias, false) || !ptr_ok(logit_offset, true) ||
+    const bool softmax = d->route_kind == MOE_ROUTE_SOFTMAX;
+    if (!ptr_ok(x, empty) || !ptr_ok(router_w, false) || !ptr_ok(bias, softmax) || !ptr_ok(logit_offset, true) ||
         !ptr_ok(y, empty) || !ptr_ok(inds_out, true) || !ptr_ok(scores_out, true))
         return MOE_ERR_INVALID;
     if (!ew || !ptr_ok(ew->w_gate, false) || !ptr_ok(ew->w_up, false) || !ptr_ok(ew->w_down, false))
@@ -246,7 +267,8 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
          !ptr_ok(ew->b_up, false) || !ptr_ok(ew->s_down, false) || !ptr_ok(ew->b_down, false)))
         return MOE_ERR_INVALID;
     if (d->I_shared > 0) {
-        if (!sw || !ptr_ok(sw->w_gate, false) || !ptr_ok(sw->w_up, false) || !ptr_ok(sw->w_down, false))
+        if (!sw || !ptr_ok(sw->w_gate, false) || !ptr_ok(sw->w_up, false) || !ptr_ok(sw->w_down, false) ||
+            !ptr_ok(sw->w_sgate, true))
             return MOE_ERR_INVALID;
     } else if (sw) {
         return MOE_ERR_INVALID;
@@ -259,6 +281,7 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     float* logits = (float*)(ws + L.logits);
+    float* sgl = (d->I_shared > 0 && sw->w_sgate) ? (float*)(ws + L.sgl) : nullptr;
     int32_t* inds = inds_out ? inds_out : (int32_t*)(ws + L.inds);
     float* scores = scores_out ? scores_out : (float*)(ws + L.scores);
     int32_t* blk = (int32_t*)(ws + L.blk);
@@ -274,7 +297,9 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
         return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 1, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_ROUTE, 0, s)))) return rc;
-    if ((rc = hip_rc(launch_route(logits, d->T, d->E, bias, d->route, inds, scores, s)))) return rc;
+    if ((rc = hip_rc(softmax ? launch_route_softmax(logits, d->T, d->E, d->route.top_k, inds, scores, s)
+                             : launch_route(logits, d->T, d->E, bias, d->route, inds, scores, s))))
+        return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_ROUTE, 1, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_DISPATCH, 0, s)))) return rc;
     if ((rc = hip_rc(launch_dispatch(inds, d->T, d->route.top_k, d->E, counts, offsets, sorted_slot, slot_row, blk,
@@ -357,7 +382,9 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
         if ((rc = hip_rc(mark(stage, 1, s)))) return rc;
     }
     if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 0, s)))) return rc;
-    if ((rc = hip_rc(launch_combine(a, d->act_dtype, scores, slot_row, y, s)))) return rc;
+    if (sgl && (rc = hip_rc(launch_router(x, sw->w_sgate, d->act_dtype, d->T, d->H, 1, nullptr, sgl, s))))
+        return rc;
+    if ((rc = hip_rc(launch_combine(a, d->act_dtype, scores, slot_row, sgl, y, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 1, s)))) return rc;
     ++g_hook.calls;
     return MOE_OK;

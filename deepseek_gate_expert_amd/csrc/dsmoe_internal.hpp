@@ -8,6 +8,29 @@
 
 namespace dsmoe {
 
+// exp by Cody & Waite range reduction with a degree-7 Taylor polynomial, evaluated with exactly
+// the fp32 operations spelled out in route.hip's header (used by the gate and by the shared-
+// expert gate in the combine, so both follow one definition)
+__device__ __forceinline__ float exp_cw(float x) {
+    if (x != x) return x;
+    if (x > 0x1.62e430p+6f) return __builtin_inff();
+    if (x < -0x1.5d589ep+6f) return 0.0f;
+    const float n = __builtin_rintf(x * 0x1.715476p+0f);
+    float r = __builtin_fmaf(-n, 0x1.62e400p-1f, x);
+    r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
+    float p = 0x1.a01a02p-13f;
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float sigmoid_cw(float x) { return 1.0f / (1.0f + exp_cw(-x)); }
+
 typedef uint16_t bf16_t;  // raw bf16 bits in memory
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -75,7 +98,11 @@ hipError_t launch_tiles(const GroupedArgs& a, int32_t BM, int32_t min_rows, int3
                         hipStream_t s);
 hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32_t g0, int32_t g1, int32_t wdt,
                              const int32_t* tile_count, const int32_t* tile_info, int32_t max_tiles, hipStream_t s);
+hipError_t launch_route_softmax(const float* logits, int64_t T, int32_t E, int32_t K, int32_t* inds, float* scores,
+                                hipStream_t s);
+// sgate_logits: NULL, or [T] fp32 logits of the shared-expert gate (the shared row is scaled by
+// their sigmoid)
 hipError_t launch_combine(const GroupedArgs& a, int32_t act, const float* scores, const int32_t* slot_row,
-                          void* y, hipStream_t s);
+                          const float* sgate_logits, void* y, hipStream_t s);
 
 }  // namespace dsmoe

@@ -1,4 +1,4 @@
-// route.hip - the DeepSeek gate, one wavefront (64 lanes) per token.
+// route.hip - the DeepSeek gate (and its softmax sibling), one wavefront (64 lanes) per token.
 //
 // Page: "feat(engine): E1 DeepSeek-style MoE gate (sigmoid, group top-k, bias) (#108)",
 // sections "API" and "Algorithm" (S1 bias selects but does not weigh, S2 norm only for
@@ -21,6 +21,10 @@
 //   4. w_j = s[inds_j]; if top_k > 1 and norm: S = ((w_0 + w_1) + w_2) + ..., w_j = w_j / S;
 //      then w_j = w_j * routed_scaling_factor.  Lane j writes output j.
 //
+// Softmax gate (mode 3): ex = exp(logit - max over the row) ranks the experts (same 64-bit
+// keys, so ties go to the lower index); w_j = ex[inds_j] / (sum of all ex), then
+// w_j = w_j / (left-to-right sum of the w_j) always; no bias, groups or scale.
+//
 // exp: Cody & Waite range reduction with a degree-7 Taylor polynomial (W. J. Cody, W. Waite,
 // "Software Manual for the Elementary Functions", 1980), evaluated with exactly these fp32
 // operations, no contraction:
@@ -36,26 +40,6 @@ namespace dsmoe {
 namespace {
 
 constexpr int WAVES = 4;  // tokens per 256-thread workgroup
-
-__device__ __forceinline__ float exp_cw(float x) {
-    if (x != x) return x;
-    if (x > 0x1.62e430p+6f) return __builtin_inff();
-    if (x < -0x1.5d589ep+6f) return 0.0f;
-    const float n = __builtin_rintf(x * 0x1.715476p+0f);
-    float r = __builtin_fmaf(-n, 0x1.62e400p-1f, x);
-    r = __builtin_fmaf(-n, 0x1.7f7d1cp-20f, r);
-    float p = 0x1.a01a02p-13f;
-    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);
-    p = __builtin_fmaf(p, r, 0x1.111112p-7f);
-    p = __builtin_fmaf(p, r, 0x1.555556p-5f);
-    p = __builtin_fmaf(p, r, 0x1.555556p-3f);
-    p = __builtin_fmaf(p, r, 0.5f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    return __builtin_ldexpf(p, (int)n);
-}
-
-__device__ __forceinline__ float sigmoid_cw(float x) { return 1.0f / (1.0f + exp_cw(-x)); }
 
 // monotone fp32 -> uint32: larger value, larger key; -0 and +0 share a key; NaN is 0 (lowest)
 __device__ __forceinline__ uint32_t vkey(float v) {
@@ -120,7 +104,7 @@ struct RouteArgs {
     int64_t T;
     int32_t E, K, G, TG, norm;
     float rsf;
-    int32_t mode;  // 0: no group masking, 1: lane-segment groups, 2: LDS groups
+    int32_t mode;  // 0: no group masking, 1: lane-segment groups, 2: LDS groups, 3: softmax gate
     int32_t L;     // lanes per group in mode 1
 };
 
@@ -134,17 +118,49 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const int32_t E = a.E;
 
     float sg[P];
-    uint32_t bk[P];  // value keys of the biased scores
+    uint32_t bk[P];  // value keys of the biased scores (softmax: of the exponentials)
+    float s_all = 0.0f;  // softmax: sum of the exponentials over all experts
+    if (a.mode != 3) {
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const int32_t e = lane * P + i;
-        if (e < E) {
-            sg[i] = sigmoid_cw(a.logits[t * E + e]);
-            bk[i] = vkey(sg[i] + a.bias[e]);
-        } else {
-            sg[i] = 0.0f;
-            bk[i] = 0u;
+        for (int i = 0; i < P; ++i) {
+            const int32_t e = lane * P + i;
+            if (e < E) {
+                sg[i] = sigmoid_cw(a.logits[t * E + e]);
+                bk[i] = vkey(sg[i] + a.bias[e]);
+            } else {
+                sg[i] = 0.0f;
+                bk[i] = 0u;
+            }
         }
+    } else {
+        // softmax gate: ex = exp(logit - max) ranks the experts; the weights are ex / sum(ex),
+        // renormalised over the selection below
+        float lg[P];
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int32_t e = lane * P + i;
+            lg[i] = e < E ? a.logits[t * E + e] : -__builtin_inff();
+            m = lg[i] > m ? lg[i] : m;
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            const float o = __shfl_xor(m, off);
+            m = o > m ? o : m;
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            if (lane * P + i < E) {
+                sg[i] = exp_cw(lg[i] - m);
+                bk[i] = vkey(sg[i]);
+                part = part + sg[i];
+            } else {
+                sg[i] = 0.0f;
+                bk[i] = 0u;
+            }
+        }
+        for (int off = 32; off > 0; off >>= 1) part = part + __shfl_xor(part, off);
+        s_all = part;
     }
 
     if (a.mode == 1) {
@@ -223,15 +239,20 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
                     key[i] = 0ull;
                 }
         }
-        const float wj = __shfl(sv, owner);
+        const float wraw = __shfl(sv, owner);
+        const float wj = a.mode == 3 ? wraw / s_all : wraw;
         S = (j == 0) ? wj : S + wj;
         if (lane == j) {
             my_e = esel;
             my_w = wj;
         }
     }
-    if (a.K > 1 && a.norm) my_w = my_w / S;
-    my_w = my_w * a.rsf;
+    if (a.mode == 3) {
+        my_w = my_w / S;  // always renormalised, no scale
+    } else {
+        if (a.K > 1 && a.norm) my_w = my_w / S;
+        my_w = my_w * a.rsf;
+    }
     if (lane < a.K) {
         a.inds[t * a.K + lane] = my_e;
         a.scores[t * a.K + lane] = my_w;
@@ -277,6 +298,34 @@ hipError_t launch_route(const float* logits, int64_t T, int32_t E, const float* 
             a.mode = 2;
         }
     }
+    switch (P) {
+        case 1: return launch_p<1>(a, s);
+        case 2: return launch_p<2>(a, s);
+        case 4: return launch_p<4>(a, s);
+        case 8: return launch_p<8>(a, s);
+        default: return launch_p<16>(a, s);
+    }
+}
+
+hipError_t launch_route_softmax(const float* logits, int64_t T, int32_t E, int32_t K, int32_t* inds, float* scores,
+                                hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    int P = 1;
+    while (64 * P < E) P *= 2;
+    RouteArgs a;
+    a.logits = logits;
+    a.bias = nullptr;
+    a.inds = inds;
+    a.scores = scores;
+    a.T = T;
+    a.E = E;
+    a.K = K;
+    a.G = 1;
+    a.TG = 1;
+    a.norm = 1;
+    a.rsf = 1.0f;
+    a.mode = 3;
+    a.L = 1;
     switch (P) {
         case 1: return launch_p<1>(a, s);
         case 2: return launch_p<2>(a, s);

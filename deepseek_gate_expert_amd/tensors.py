@@ -12,8 +12,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_OK, MOE_Q4G64, LayerDesc, layer_desc, moe_forward,
-               moe_forward_workspace_size, moe_strerror)
+from . import (MOE_BF16, MOE_F32, MOE_OK, MOE_Q4G64, MOE_ROUTE_DEEPSEEK, MOE_ROUTE_SOFTMAX, LayerDesc, layer_desc,
+               moe_forward, moe_forward_workspace_size, moe_strerror)
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "q4": MOE_Q4G64}
 
@@ -87,15 +87,19 @@ class DeviceLayer:
 
 def make_desc(w, T: Optional[int] = None) -> LayerDesc:
     """Layer descriptor from a workload-like object (fields T,H,E,I,Is,K,G,TG,norm,rsf,act,expert)."""
+    kind = MOE_ROUTE_SOFTMAX if getattr(w, "route", "deepseek") == "softmax" else MOE_ROUTE_DEEPSEEK
     return layer_desc(w.T if T is None else T, w.H, w.E, w.I, w.Is, _DT[w.act], _DT[w.expert], w.K, w.G, w.TG,
-                      w.norm, w.rsf)
+                      w.norm, w.rsf, kind)
 
 
 def upload_layer(w, router: np.ndarray, bias: np.ndarray, experts: dict, shared: Optional[dict],
-                 offset: Optional[np.ndarray], device, T: Optional[int] = None) -> DeviceLayer:
+                 offset: Optional[np.ndarray], device, T: Optional[int] = None,
+                 shared_gate: Optional[np.ndarray] = None) -> DeviceLayer:
     dev = torch.device(device)
     ex = {k: to_device(v, dev) for k, v in experts.items()}
     sh = None if shared is None else {k: to_device(v, dev) for k, v in shared.items()}
+    if sh is not None and shared_gate is not None:
+        sh["sgate"] = to_device(shared_gate, dev)
     off = None if offset is None else to_device(np.ascontiguousarray(offset, np.float32), dev)
     return DeviceLayer(make_desc(w, T), to_device(router, dev), to_device(np.ascontiguousarray(bias, np.float32), dev),
                        ex, sh, off)

@@ -51,6 +51,10 @@ extern "C" {
 #define MOE_BF16 1  /* bfloat16 (uint16 bit patterns) */
 #define MOE_Q4G64 2 /* 4-bit affine, groups of 64 along the input axis (expert weights only) */
 
+/* gate kinds (moe_layer_desc.route_kind) */
+#define MOE_ROUTE_DEEPSEEK 0 /* sigmoid gate with correction bias and groups (moe_route_deepseek) */
+#define MOE_ROUTE_SOFTMAX 1  /* softmax gate, always renormalised (moe_route_softmax) */
+
 /* implementation limits (-4 beyond them) */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOP_K 64
@@ -73,7 +77,8 @@ typedef struct moe_layer_desc {
     int32_t I_shared;    /* shared expert intermediate size; 0 = no shared expert */
     int32_t act_dtype;   /* MOE_F32 or MOE_BF16: x, y, router weight and shared weights */
     int32_t expert_dtype;/* MOE_F32 (with act F32), MOE_BF16 or MOE_Q4G64 (with act BF16) */
-    moe_route_params route;
+    moe_route_params route; /* the softmax gate reads only route.top_k */
+    int32_t route_kind;  /* MOE_ROUTE_DEEPSEEK or MOE_ROUTE_SOFTMAX */
 } moe_layer_desc;
 
 /* Routed expert weights, stacked along E.
@@ -94,11 +99,16 @@ typedef struct moe_expert_weights {
 } moe_expert_weights;
 
 /* Shared expert ([Epic56] "Decision 5" item 2: always active, weight 1, no gate):
- * w_gate, w_up [I_shared, H]; w_down [H, I_shared]; act_dtype. */
+ * w_gate, w_up [I_shared, H]; w_down [H, I_shared]; act_dtype.
+ * w_sgate: NULL (the DeepSeek body: weight 1), or [H] act_dtype: the shared expert's output of
+ * token t is scaled by sigmoid(x[t] . w_sgate) -- the combine's shared-expert gate switch that
+ * [PR123]'s reviews name (the dot product in moe_router_logits' order, the sigmoid as in the
+ * gate). */
 typedef struct moe_shared_weights {
     const void* w_gate;
     const void* w_up;
     const void* w_down;
+    const void* w_sgate;
 } moe_shared_weights;
 
 /*
@@ -138,6 +148,22 @@ int moe_route_deepseek(const float* logits, int64_t T, int32_t E, const float* b
                        const moe_route_params* p, int32_t* inds, float* scores, void* stream);
 
 /*
+ * Softmax gate, the DeepSeek route's sibling ([PR123] "API": same output contract; second
+ * review, S2: its weights are renormalised in every case, unlike the DeepSeek route's
+ * top_k > 1 guard).  The pages define nothing further; this implementation, one row per token:
+ *   ex_e = exp(logit_e - max_e logit_e) in fp32 (the gate's exp);
+ *   inds = the top_k experts by ex, ordered by ex descending then index ascending;
+ *   p_j = ex[inds_j] / sum_e ex_e;  scores_j = p_j / (left-to-right sum of the p_j).
+ * No bias, groups or scaling factor.  The sum over all experts is formed in a fixed tree order
+ * (it cancels in the renormalisation up to rounding).
+ *   logits: fp32 [T, E] (device)   inds: int32 [T, top_k]   scores: fp32 [T, top_k] (written)
+ * Errors: -1 for NULL pointers, T < 0, E < 1, top_k outside [1, E], misaligned pointers;
+ * -4 for E > MOE_MAX_EXPERTS or top_k > MOE_MAX_TOP_K.
+ */
+int moe_route_softmax(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* inds, float* scores,
+                      void* stream);
+
+/*
  * Dispatch (the grouping behind gather_mm / gather_qmm, [Epic56] opening paragraph): a stable
  * counting sort of the T*K token slots (slot s = t*K + j) by expert.
  *   counts[e]      = number of slots routed to e                          int32 [E]
@@ -158,21 +184,24 @@ int moe_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* 
 /*
  * Whole layer ([Epic56] forwardMoeWith; [PR123] merge recommendation: router -> route ->
  * switch_glu -> combine, shared expert always active, no shared-expert gate):
- *   y[t] = shared(x[t]) + sum_{j<K} scores[t,j] * expert_{inds[t,j]}(x[t])
+ *   y[t] = g_t * shared(x[t]) + sum_{j<K} scores[t,j] * expert_{inds[t,j]}(x[t])
+ *   (g_t = 1, or sigmoid(x[t] . w_sgate) when the shared weights carry a gate vector)
  *   expert(x) = W_down (silu(W_gate x) * (W_up x))   (SwiGLU; the gate projection is the one
  *                                                      that goes through silu)
- * Steps, all on `stream`: router logits (as moe_router_logits) -> gate (as moe_route_deepseek)
- * -> dispatch (as moe_dispatch) -> grouped gate/up GEMM with SwiGLU in the epilogue -> grouped
- * down GEMM -> combine.  For bf16 and 4-bit layers with T > 64, each grouped GEMM is two
- * kernels: weight streaming for the expert groups of at most 64 rows, MFMA tiles for the
- * larger groups and the shared expert.  The combine adds, per token and output element, the shared expert's
- * output and then the K weighted expert outputs in j order in fp32, with no atomics.
+ * Steps, all on `stream`: router logits (as moe_router_logits) -> gate (as moe_route_deepseek,
+ * or moe_route_softmax when route_kind is MOE_ROUTE_SOFTMAX) -> dispatch (as moe_dispatch) ->
+ * grouped gate/up GEMM with SwiGLU in the epilogue -> grouped down GEMM -> combine.  For bf16
+ * and 4-bit layers with T > 64, each grouped GEMM is two kernels: weight streaming for the
+ * expert groups of at most 64 rows, MFMA tiles for the larger groups and the shared expert.
+ * The combine adds, per token and output element, the (gated) shared expert's output and then
+ * the K weighted expert outputs in j order in fp32, with no atomics.
  * Precision: bf16 layers run bf16 MFMA with fp32 accumulation; the SwiGLU intermediate and the
  * per-expert outputs are rounded to bf16; y is rounded to act_dtype (nearest-even).  4-bit
  * weights are dequantised in registers (s*q + b, rounded to bf16) before the MFMA.
  *   d:            shapes, dtypes and gate parameters (host)
  *   x:            [T, H] act_dtype (device)          router_w: [E, H] act_dtype (device)
- *   bias:         fp32 [E] (device)                  logit_offset: NULL or fp32 [E] (device),
+ *   bias:         fp32 [E] (device; may be NULL with the softmax gate)
+ *   logit_offset: NULL or fp32 [E] (device),
  *                 added to the router logits (a router bias; NULL for DeepSeek checkpoints)
  *   ew:           routed expert weights (host struct of device pointers)
  *   sw:           shared expert weights (host struct of device pointers); NULL iff I_shared == 0

@@ -192,3 +192,51 @@ def test_workspace_grows_with_tokens(lib):
     a = lib.moe_forward_workspace_size(ctypes.byref(desc(T=16)))
     b = lib.moe_forward_workspace_size(ctypes.byref(desc(T=1024)))
     assert b > a > 0
+
+
+def route_softmax(lib, T=4, E=8, K=2, logits=P, inds=P, scores=P):
+    return lib.moe_route_softmax(logits, T, E, K, inds, scores, None)
+
+
+SOFTMAX_REJECTS = {
+    "top_k_zero": dict(K=0),
+    "top_k_gt_E": dict(K=9),
+    "zero_E": dict(E=0, K=1),
+    "negative_T": dict(T=-1),
+    "null_logits": dict(logits=None),
+    "null_inds": dict(inds=None),
+    "null_scores": dict(scores=None),
+    "misaligned_scores": dict(scores=P + 4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SOFTMAX_REJECTS))
+def test_route_softmax_reject_matrix(lib, name):
+    assert route_softmax(lib, **SOFTMAX_REJECTS[name]) == dg.MOE_ERR_INVALID
+
+
+def test_route_softmax_limits_and_empty(lib):
+    assert route_softmax(lib, E=2048, K=2) == dg.MOE_ERR_UNSUPPORTED
+    assert route_softmax(lib, E=256, K=65) == dg.MOE_ERR_UNSUPPORTED
+    assert route_softmax(lib, T=0, logits=None, inds=None, scores=None) == dg.MOE_OK
+
+
+def _forward_raw(lib, d, bias=P, sgate=None, shared=True):
+    ew = dg.ExpertWeights(P, P, P)
+    sw = dg.SharedWeights(P, P, P, sgate) if shared else None
+    need = lib.moe_forward_workspace_size(ctypes.byref(d))
+    return lib.moe_forward(ctypes.byref(d), None, P, bias, None, ctypes.byref(ew),
+                           None if sw is None else ctypes.byref(sw), None, None, None, P, need, None)
+
+
+def test_forward_route_kind_validation(lib):
+    # T = 0 passes validation without touching the GPU, so only the checks are exercised
+    soft = dict(T=0, route_kind=dg.MOE_ROUTE_SOFTMAX)
+    assert _forward_raw(lib, desc(**soft), bias=None) == dg.MOE_OK           # bias optional for softmax
+    assert _forward_raw(lib, desc(T=0), bias=None) == dg.MOE_ERR_INVALID     # required for the DeepSeek gate
+    assert _forward_raw(lib, desc(**soft, n_group=3), bias=None) == dg.MOE_OK  # group params ignored
+    assert _forward_raw(lib, desc(**soft, top_k=9)) == dg.MOE_ERR_INVALID
+    assert _forward_raw(lib, desc(**soft, top_k=65, E=128)) == dg.MOE_ERR_UNSUPPORTED
+    assert _forward_raw(lib, desc(T=0, route_kind=2)) == dg.MOE_ERR_INVALID
+    assert _forward_raw(lib, desc(T=0), sgate=P) == dg.MOE_OK
+    assert _forward_raw(lib, desc(T=0), sgate=P + 2) == dg.MOE_ERR_INVALID  # misaligned gate vector

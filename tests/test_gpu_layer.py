@@ -73,7 +73,7 @@ def small_case(w, seed_shift=0):
 
 
 def run_small(w, r, b, x, ex, sh, off):
-    layer = upload_layer(w, r, b, ex, sh if w.Is > 0 else None, off, DEV)
+    layer = upload_layer(w, r, b, ex, sh if w.Is > 0 else None, off, DEV, shared_gate=synth.gen_shared_gate(w))
     y, inds, scores = layer(to_device(x, DEV), want_route=True)
     torch.cuda.synchronize()
     return y, inds.cpu().numpy(), scores.cpu().numpy()
@@ -103,6 +103,14 @@ EDGE = [
     ("tiled_rows256_q4", C1.with_(T=2048, H=256, I=128, Is=128, expert="q4", planted=0)),
     ("tiled_1024_experts_shared", C1.with_(T=100, H=128, I=64, Is=64, E=1024, K=2, G=1, TG=1, planted=0)),
     ("tiled_skewed", C1.with_(T=1500, H=192, I=128, Is=64, zipf_s=2.0, planted=0)),
+    # softmax gate and sigmoid-gated shared expert
+    ("softmax_streamed", C1.with_(T=48, route="softmax", planted=0)),
+    ("softmax_tiled", C1.with_(T=600, H=256, I=128, Is=128, route="softmax", planted=0)),
+    ("shared_gate_streamed", C1.with_(T=40, shared_gate=True, planted=0)),
+    ("shared_gate_tiled_router", C1.with_(T=700, H=256, I=128, Is=128, shared_gate=True, planted=0)),
+    ("softmax_gated_q4", C1.with_(T=300, H=256, I=128, Is=128, expert="q4", route="softmax", shared_gate=True,
+                                  planted=0)),
+    ("softmax_gated_f32", synth.WORKLOADS["c0"].with_(route="softmax", shared_gate=True)),
 ]
 
 
@@ -112,7 +120,8 @@ def test_layer_edge_cases(label, w):
     args = small_case(w)
     y, gi, gs = run_small(*args)
     w_, r, b, x, ex, sh, off = args
-    y_ref, oi, os_, _ = oracle.forward_workload(w_, x, r, b, ex, sh if w_.Is > 0 else None, offset=off)
+    y_ref, oi, os_, _ = oracle.forward_workload(w_, x, r, b, ex, sh if w_.Is > 0 else None, offset=off,
+                                                shared_gate=synth.gen_shared_gate(w_))
     check_route(gi, gs, oi, os_)
     err = rel_l2(act_to_f64(y), y_ref)
     log(f"[edge] {label} rel L2 {err:.3e}")

@@ -158,3 +158,74 @@ def test_route_rejects_leave_outputs_untouched():
     assert dg.moe_route_deepseek(lg, good, inds, scores, 2, 2, 3) == dg.MOE_ERR_INVALID
     torch.cuda.synchronize()
     assert bool((inds == -7).all()) and bool((scores == -7.0).all())
+
+
+# ---- softmax gate (moe_route_softmax) --------------------------------------------------------
+
+def run_gpu_softmax(logits: np.ndarray, K):
+    T = logits.shape[0]
+    lg = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).to(DEV)
+    inds = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    scores = torch.full((T, K), -7.0, dtype=torch.float32, device=DEV)
+    rc = dg.moe_route_softmax(lg, inds, scores, K)
+    torch.cuda.synchronize()
+    return rc, inds.cpu().numpy(), scores.cpu().numpy()
+
+
+SOFTMAX_SHAPES = [
+    # T,   E,    K,  logit_std
+    (16, 8, 2, 1.0),
+    (512, 64, 6, 1.0),
+    (64, 256, 8, 1.0),
+    (4096, 256, 8, 2.0),
+    (37, 200, 5, 3.0),     # E not a multiple of 64
+    (19, 1000, 7, 1.0),    # 16 experts per lane
+    (9, 128, 1, 1.0),      # top_k = 1: weights exactly 1
+    (9, 48, 48, 1.0),      # top_k = E
+    (7, 64, 64, 0.5),      # top_k = 64 (limit)
+    (3, 1, 1, 1.0),        # a single expert
+]
+
+
+@pytest.mark.parametrize("T,E,K,std", SOFTMAX_SHAPES, ids=[f"T{s[0]}E{s[1]}K{s[2]}" for s in SOFTMAX_SHAPES])
+def test_route_softmax_matches_oracle(T, E, K, std):
+    log(f"[route-softmax] T={T} E={E} K={K}")
+    seed = T * 7919 + E * 31 + K + 17
+    logits = synth.normal_f32(seed, 1, T * E, std).reshape(T, E)
+    rc, gi, gs = run_gpu_softmax(logits, K)
+    assert rc == 0, dg.moe_strerror(rc)
+    orc, oi, os_ = oracle.route_softmax(logits, K)
+    assert orc == 0
+    assert np.array_equal(gi, oi)
+    den = np.maximum(np.abs(os_.astype(np.float64)), 1e-30)
+    assert np.max(np.abs(gs.astype(np.float64) - os_) / den) <= 1e-6
+    if K == 1:
+        assert np.all(gs == 1.0)
+
+
+def test_route_softmax_ties_and_large_logits():
+    # equal logits: the lowest indices win and the weights are exactly 1/K; a row shifted by 1000
+    # (exp(l - max) never overflows) and a row with one dominant logit
+    E, K = 64, 4
+    lg = np.zeros((3, E), np.float32)
+    lg[0, :] = 2.5
+    lg[1, :] = 1000.0 + synth.normal_f32(3, 1, E, 1.0)
+    lg[2, :] = -5.0
+    lg[2, 17] = 80.0
+    rc, gi, gs = run_gpu_softmax(lg, K)
+    assert rc == 0
+    orc, oi, os_ = oracle.route_softmax(lg, K)
+    assert np.array_equal(gi, oi)
+    assert list(gi[0]) == [0, 1, 2, 3] and np.all(gs[0] == 0.25)
+    assert gi[2, 0] == 17 and np.all(np.isfinite(gs))
+    np.testing.assert_allclose(gs, os_, rtol=1e-6, atol=0)
+
+
+def test_route_softmax_rejects_leave_outputs_untouched():
+    lg = torch.zeros((4, 8), dtype=torch.float32, device=DEV)
+    inds = torch.full((4, 2), -7, dtype=torch.int32, device=DEV)
+    scores = torch.full((4, 2), -7.0, dtype=torch.float32, device=DEV)
+    assert dg.moe_route_softmax(lg, inds, scores, 0) == dg.MOE_ERR_INVALID
+    assert dg.moe_route_softmax(lg, inds, scores, 9) == dg.MOE_ERR_INVALID
+    torch.cuda.synchronize()
+    assert torch.all(inds == -7) and torch.all(scores == -7.0)
