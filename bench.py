@@ -46,7 +46,9 @@ class HipEvents:
     """hipEvent_t handles created through the HIP runtime (timing enabled)."""
 
     def __init__(self, n: int):
-        self.hip = ctypes.CDLL("libamdhip64.so")
+        # the HIP runtime torch has loaded (torch ships its own copy): events must come from it
+        mapped = [ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln]
+        self.hip = ctypes.CDLL(mapped[0] if mapped else "libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
@@ -175,6 +177,60 @@ def run_workload(name: str, steps: int, warmup: int, cache: dict):
                 x=x, bias=bias, offset=offset, router=router, experts=experts, shared=shared)
 
 
+def run_dense(steps: int, warmup: int):
+    """DeepSeek-V3 dense SwiGLU layer (H 7168, I 18432) on 8192 tokens, bf16."""
+    import numpy as np
+    import torch
+
+    import synth
+    import deepseek_gate_expert_amd as dg
+    from deepseek_gate_expert_amd.tensors import to_device
+
+    T, H, I = 8192, 7168, 18432
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    x = synth.normal_bf16(5, synth.TID_X, T * H, 1.0).reshape(T, H)
+    wg = synth.normal_bf16(2, 13, I * H, 1 / np.sqrt(H)).reshape(I, H)
+    wu = synth.normal_bf16(2, 14, I * H, 1 / np.sqrt(H)).reshape(I, H)
+    wd = synth.normal_bf16(2, 15, H * I, 1 / np.sqrt(I)).reshape(H, I)
+    log(f"[bench] generated dense weights in {time.time() - t0:.1f}s")
+    xd, g, u, d = (to_device(a, dev) for a in (x, wg, wu, wd))
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(dg.moe_dense_workspace_size(T, H, I, dg.MOE_BF16), dtype=torch.uint8, device=dev)
+
+    def step():
+        rc = dg.moe_dense_mlp(xd, g, u, d, y, ws)
+        if rc != 0:
+            raise RuntimeError(f"moe_dense_mlp failed: {dg.moe_strerror(rc)}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream()
+    ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    ev.hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        step()
+    ev.hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / steps
+    ev.close()
+    flops = 6.0 * T * H * I
+    ach = flops / (ms / 1e3) / 1e12
+    log(f"[bench] dense: {ms:.3f} ms/step, {ach:.0f} TFLOP/s")
+    return {"metric": "dense SwiGLU MLP tokens/sec (DeepSeek-V3 dense layer shape, bf16) + % MFMA peak",
+            "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": f"dense SwiGLU layer, T={T} H={H} I={I}, bf16", "global_batch": T,
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                         "kernel": "whole dense layer: gemm_dma<256, true> (gate/up + SwiGLU) and "
+                                   "gemm_dma<256, false> (down)"}}
+
+
 def cpu_baseline(res, budget_s: float):
     """The oracle as it stands on the host cores, on the first n tokens of the same workload
     (n grown until about `budget_s` seconds of CPU work)."""
@@ -203,7 +259,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4"])
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "dense"],
+                    help="c3: DSV3 prefill (headline); c2: decode; c4: 4-bit experts; dense: DSV3 dense MLP layer")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode batch")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     args = ap.parse_args()
@@ -224,6 +281,10 @@ def main():
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
     del cal_src, cal_dst
+
+    if args.workload == "dense":
+        print(json.dumps(run_dense(args.steps, args.warmup)))
+        return
 
     cache = {}
     main_res = run_workload(args.workload, args.steps, args.warmup, cache)

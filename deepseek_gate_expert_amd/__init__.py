@@ -27,7 +27,8 @@ MOE_MAX_EXPERTS, MOE_MAX_TOP_K = 1024, 64
 MOE_ROUTE_DEEPSEEK, MOE_ROUTE_SOFTMAX = 0, 1
 MOE_STAGE_ROUTER, MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = range(6)
 EXPORTS = ("moe_router_logits", "moe_route_deepseek", "moe_route_softmax", "moe_dispatch_workspace_size", "moe_dispatch",
-           "moe_forward_workspace_size", "moe_forward", "moe_set_stage_events", "moe_strerror")
+           "moe_forward_workspace_size", "moe_forward", "moe_dense_workspace_size", "moe_dense_mlp",
+           "moe_set_stage_events", "moe_strerror")
 
 
 class RouteParams(ctypes.Structure):
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.moe_router_logits.argtypes = [p, p, i32, i64, i32, i32, p, p, p]
         lib.moe_route_deepseek.restype = ctypes.c_int
         lib.moe_route_deepseek.argtypes = [p, i64, i32, p, i64, ctypes.POINTER(RouteParams), p, p, p]
+        lib.moe_dense_workspace_size.restype = sz
+        lib.moe_dense_workspace_size.argtypes = [i64, i32, i32, i32]
+        lib.moe_dense_mlp.restype = ctypes.c_int
+        lib.moe_dense_mlp.argtypes = [i64, i32, i32, i32, p, p, p, p, p, p, sz, p]
         lib.moe_route_softmax.restype = ctypes.c_int
         lib.moe_route_softmax.argtypes = [p, i64, i32, i32, p, p, p]
         lib.moe_dispatch_workspace_size.restype = sz
@@ -245,6 +250,36 @@ def moe_forward(desc: LayerDesc, x, router_w, bias, experts: dict, shared: Optio
     return load_library().moe_forward(ctypes.byref(desc), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(logit_offset),
                                       ctypes.byref(ew), None if sw is None else ctypes.byref(sw), _ptr(y),
                                       _ptr(inds_out), _ptr(scores_out), _ptr(workspace), nbytes, _stream(stream))
+
+
+def moe_dense_workspace_size(T: int, H: int, I: int, act_dtype: int) -> int:
+    return int(load_library().moe_dense_workspace_size(int(T), int(H), int(I), int(act_dtype)))
+
+
+def moe_dense_mlp(x, w_gate, w_up, w_down, y, workspace=None, stream=None) -> int:
+    """Dense SwiGLU MLP (see dsmoe.h): x, y [T, H]; w_gate, w_up [I, H]; w_down [H, I]; one
+    activation dtype.  Allocates the workspace when none is given."""
+    import torch
+    if x.dim() != 2 or w_gate.dim() != 2 or w_up.shape != w_gate.shape or w_down.dim() != 2:
+        return MOE_ERR_INVALID
+    T, H = x.shape
+    I = w_gate.shape[0]
+    if w_gate.shape[1] != H or tuple(w_down.shape) != (H, I) or tuple(y.shape) != (T, H):
+        return MOE_ERR_INVALID
+    if len({t.dtype for t in (x, w_gate, w_up, w_down, y)}) != 1:
+        return MOE_ERR_INVALID
+    if not _contig(x, w_gate, w_up, w_down, y, workspace) or not _same_device(x, w_gate, w_up, w_down, y, workspace):
+        return MOE_ERR_INVALID
+    act = act_code(x.dtype)
+    if workspace is None:
+        need = moe_dense_workspace_size(T, H, I, act)
+        if need == 0:
+            return load_library().moe_dense_mlp(T, H, I, act, _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                                _ptr(y), None, 0, _stream(stream))
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    return load_library().moe_dense_mlp(T, H, I, act, _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
+                                        _ptr(workspace), nbytes, _stream(stream))
 
 
 def moe_set_stage_events(stage: int, events, n_pairs: int) -> int:

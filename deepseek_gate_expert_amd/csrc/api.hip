@@ -150,6 +150,32 @@ int tiled_state() {
     return g_tiled_state[dev];
 }
 
+// Dense SwiGLU MLP: the shared-expert path on its own (group E with E = 0 routed experts).
+struct DenseLayout {
+    size_t tiles, h, total;
+};
+
+int32_t dense_bm(int64_t T, bool allow256) { return (allow256 && T >= 192) ? 256 : 128; }
+
+DenseLayout dense_layout(int64_t T, int32_t I, int32_t act) {
+    DenseLayout L;
+    const size_t el = act == MOE_F32 ? 4 : 2;
+    size_t off = 0;
+    L.tiles = off;
+    off += up(256 + 8 * (size_t)tiled_max_tiles(T, 0, 0, 128));
+    L.h = off;
+    off += up((size_t)T * (size_t)I * el);
+    L.total = off;
+    return L;
+}
+
+int check_dense(int64_t T, int32_t H, int32_t I, int32_t act) {
+    if (T < 0 || H < 1 || I < 1 || (act != MOE_F32 && act != MOE_BF16)) return MOE_ERR_INVALID;
+    if (act == MOE_BF16 && (H % 64 || I % 64)) return MOE_ERR_UNSUPPORTED;
+    if (T >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 // measurement hook state (see moe_set_stage_events)
 struct StageHook {
     int32_t stage = -1;
@@ -169,6 +195,66 @@ inline hipError_t mark(int32_t stage, int edge, hipStream_t s) {
 }  // namespace
 
 extern "C" {
+
+size_t moe_dense_workspace_size(int64_t T, int32_t H, int32_t I, int32_t act_dtype) {
+    if (check_dense(T, H, I, act_dtype) != MOE_OK) return 0;
+    return dense_layout(T, I, act_dtype).total;
+}
+
+int moe_dense_mlp(int64_t T, int32_t H, int32_t I, int32_t act_dtype, const void* x, const void* w_gate,
+                  const void* w_up, const void* w_down, void* y, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    int rc = check_dense(T, H, I, act_dtype);
+    if (rc != MOE_OK) return rc;
+    const bool empty = T == 0;
+    if (!ptr_ok(x, empty) || !ptr_ok(y, empty) || !ptr_ok(w_gate, false) || !ptr_ok(w_up, false) ||
+        !ptr_ok(w_down, false))
+        return MOE_ERR_INVALID;
+    const DenseLayout L = dense_layout(T, I, act_dtype);
+    if (!ptr_ok(workspace, false) || ((uintptr_t)workspace & (ALIGN - 1))) return MOE_ERR_INVALID;
+    if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (empty) return MOE_OK;
+
+    hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    GroupedArgs a;
+    memset(&a, 0, sizeof(a));
+    a.T = T;
+    a.H = H;
+    a.E = 0;
+    a.I = 0;
+    a.Is = I;
+    a.K = 0;
+    a.TK = 0;
+    a.ldh = I;
+    a.x = x;
+    a.h = ws + L.h;
+    a.o = y;  // row TK + t of the expert-output space is token t: the down projection writes y
+    a.swg = w_gate;
+    a.swu = w_up;
+    a.swd = w_down;
+    if (act_dtype == MOE_F32) {
+        if ((rc = hip_rc(launch_gemm1_f32(a, s)))) return rc;
+        return hip_rc(launch_gemm2_f32(a, s));
+    }
+    const int ts = tiled_state();
+    const int64_t lim = (int64_t)1 << 31;
+    const bool tiled = ts != 3 && T > STREAM_MAX_ROWS && T * (int64_t)H < lim && T * (int64_t)I < lim &&
+                       (int64_t)I * H < lim;
+    a.stream_max_rows = tiled ? STREAM_MAX_ROWS : 0x7fffffff;
+    if (!tiled) {
+        if ((rc = hip_rc(launch_gemm1_bf16(a, 0, 1, MOE_BF16, s)))) return rc;
+        return hip_rc(launch_gemm2_bf16(a, 0, 1, MOE_BF16, s));
+    }
+    const int32_t BM = dense_bm(T, ts == 1);
+    const int32_t max_tiles = tiled_max_tiles(T, 0, 0, BM);
+    int32_t* tile_count = (int32_t*)(ws + L.tiles);
+    int32_t* tile_info = tile_count + 64;
+    if ((rc = hip_rc(launch_tiles(a, BM, STREAM_MAX_ROWS, tile_count, tile_info, s)))) return rc;
+    if ((rc = hip_rc(launch_gemm_tiled(a, true, BM, 0, 1, MOE_BF16, tile_count, tile_info, max_tiles, s))))
+        return rc;
+    return hip_rc(launch_gemm_tiled(a, false, BM, 0, 1, MOE_BF16, tile_count, tile_info, max_tiles, s));
+}
 
 int moe_set_stage_events(int32_t stage, void* const* events, int32_t n_pairs) {
     if (stage < -1 || stage > MOE_STAGE_COMBINE || n_pairs < 0 || (n_pairs > 0 && !events && stage >= 0))

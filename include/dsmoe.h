@@ -221,6 +221,25 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
                 int32_t* inds_out, float* scores_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dense SwiGLU MLP layer: y = W_down (silu(W_gate x) * (W_up x)) per token -- the dense layers
+ * that DeepSeek models interleave with MoE layers ([Epic56] "Decision 5 superseded" item 2:
+ * dense/MoE layer mixing); the computation is the shared expert's path on its own, with the same
+ * kernels (weight streaming for T <= 64, MFMA tiles above) and the same precision (bf16 MFMA with
+ * fp32 accumulation, the SwiGLU intermediate rounded to bf16; fp32 layers in fp32).
+ *   x:  [T, H] act_dtype (device)        y: [T, H] act_dtype (device, written)
+ *   w_gate, w_up: [I, H]; w_down: [H, I]; act_dtype (device)
+ *   workspace: device scratch, at least moe_dense_workspace_size(T, H, I, act_dtype) bytes,
+ *              256-byte aligned
+ * Errors: -1 for T < 0, H < 1, I < 1, act_dtype other than MOE_F32 / MOE_BF16, NULL or
+ * misaligned pointers; -3 for a small workspace; -4 for bf16 with H or I not a multiple of 64,
+ * or T >= 2^31.  moe_dense_workspace_size returns 0 for arguments moe_dense_mlp would reject.
+ */
+size_t moe_dense_workspace_size(int64_t T, int32_t H, int32_t I, int32_t act_dtype);
+int moe_dense_mlp(int64_t T, int32_t H, int32_t I, int32_t act_dtype, const void* x, const void* w_gate,
+                  const void* w_up, const void* w_down, void* y, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
  * Measurement hook (not part of the computation).  Stages of moe_forward, in launch order:
  *   MOE_STAGE_ROUTER (router logits), MOE_STAGE_ROUTE (gate), MOE_STAGE_DISPATCH (count, scan,
  *   scatter), MOE_STAGE_GEMM1 (gate/up + SwiGLU), MOE_STAGE_GEMM2 (down), MOE_STAGE_COMBINE.

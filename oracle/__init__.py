@@ -79,6 +79,8 @@ def _L():
         lib.oracle_swiglu.argtypes = [p, i32, i32, i32] + [p] * 9 + [p]
         lib.oracle_forward.restype = ctypes.c_int
         lib.oracle_forward.argtypes = [ctypes.POINTER(Layer), p, i64, p, p, p, p]
+        lib.oracle_dense_mlp.restype = ctypes.c_int
+        lib.oracle_dense_mlp.argtypes = [p, i32, i64, i32, i32, p, p, p, p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -160,6 +162,19 @@ def swiglu(x: np.ndarray, wg, wu, wd, dtype: str, q4: Optional[dict] = None) -> 
                        *[_p(q4.get(k)) for k in ("s_gate", "b_gate", "s_up", "b_up", "s_down", "b_down")],
                        _p(out))
     return out
+
+
+def dense_mlp(x, wg, wu, wd, act: str) -> np.ndarray:
+    """Dense SwiGLU MLP layer on every row of x; fp64 [T, H]."""
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    I = wg.shape[0]
+    y = np.empty((T, H), np.float64)
+    keep = [np.ascontiguousarray(a) for a in (wg, wu, wd)]
+    rc = _L().oracle_dense_mlp(_p(x), _DT[act], T, H, I, *[_p(a) for a in keep], _p(y))
+    if rc != 0:
+        raise ValueError(f"oracle_dense_mlp rejected its arguments (rc={rc})")
+    return y
 
 
 def forward(x, router_w, bias, experts: dict, shared: Optional[dict], *, T, H, E, I, Is, K, G, TG, norm,

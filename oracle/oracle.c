@@ -389,6 +389,25 @@ int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, d
     return 0;
 }
 
+/* Dense SwiGLU MLP layer ([Epic56] "Decision 5 superseded" item 2: DeepSeek mixes dense and MoE
+ * layers): y[t] = W_down (silu(W_gate x_t) * (W_up x_t)) for every token, fp64 (oracle_swiglu
+ * on each row).  Returns 0, or -1 on invalid arguments. */
+int oracle_dense_mlp(const void* x, int32_t act, int64_t T, int32_t H, int32_t I, const void* wg, const void* wu,
+                     const void* wd, double* y) {
+    if (!x || !wg || !wu || !wd || !y || T < 0 || H < 1 || I < 1 || (act != 0 && act != 1)) return -1;
+#pragma omp parallel
+    {
+        double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int32_t k = 0; k < H; ++k) xd[k] = (double)act_at(x, act, t * (int64_t)H + k);
+            oracle_swiglu(xd, H, I, act, wg, wu, wd, NULL, NULL, NULL, NULL, NULL, NULL, y + t * (int64_t)H);
+        }
+        free(xd);
+    }
+    return 0;
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif

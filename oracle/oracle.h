@@ -88,6 +88,10 @@ void oracle_swiglu(const double* x, int32_t H, int32_t I, int32_t dtype, const v
 int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, double* y, int32_t* inds,
                    float* scores, float* logits);
 
+/* Dense SwiGLU MLP over T rows of x ([T,H] act), weights [I,H], [I,H], [H,I] in act; y fp64 [T,H].
+ * Returns 0, or -1 on invalid arguments. */
+int oracle_dense_mlp(const void* x, int32_t act, int64_t T, int32_t H, int32_t I, const void* wg, const void* wu,
+                     const void* wd, double* y);
 /* host threads used by the OpenMP loops */
 int oracle_num_threads(void);
 

@@ -240,3 +240,20 @@ def test_forward_route_kind_validation(lib):
     assert _forward_raw(lib, desc(T=0, route_kind=2)) == dg.MOE_ERR_INVALID
     assert _forward_raw(lib, desc(T=0), sgate=P) == dg.MOE_OK
     assert _forward_raw(lib, desc(T=0), sgate=P + 2) == dg.MOE_ERR_INVALID  # misaligned gate vector
+
+
+def test_dense_rejects(lib):
+    f = lib.moe_dense_mlp
+    need = lib.moe_dense_workspace_size(16, 128, 64, 1)
+    assert need > 0
+    assert lib.moe_dense_workspace_size(16, 96, 64, 1) == 0      # bf16 needs multiples of 64
+    assert lib.moe_dense_workspace_size(-1, 128, 64, 1) == 0
+    assert f(16, 128, 64, 1, None, P, P, P, P, P, need, None) == dg.MOE_ERR_INVALID
+    assert f(16, 128, 64, 1, P, None, P, P, P, P, need, None) == dg.MOE_ERR_INVALID
+    assert f(16, 128, 64, 1, P, P, P, P, None, P, need, None) == dg.MOE_ERR_INVALID
+    assert f(16, 128, 64, 5, P, P, P, P, P, P, need, None) == dg.MOE_ERR_INVALID
+    assert f(16, 0, 64, 1, P, P, P, P, P, P, need, None) == dg.MOE_ERR_INVALID
+    assert f(16, 128, 64, 1, P, P, P, P, P, P + 16, need, None) == dg.MOE_ERR_INVALID  # misaligned workspace
+    assert f(16, 128, 64, 1, P, P, P, P, P, P, need - 1, None) == dg.MOE_ERR_WORKSPACE
+    assert f(16, 96, 64, 1, P, P, P, P, P, P, need, None) == dg.MOE_ERR_UNSUPPORTED
+    assert f(0, 128, 64, 1, None, P, P, P, None, P, need, None) == dg.MOE_OK
