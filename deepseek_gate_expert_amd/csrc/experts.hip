@@ -171,7 +171,7 @@ __device__ __forceinline__ void s_wait_barrier() { asm volatile("s_waitcnt vmcnt
 // N is a multiple of 64 (bf16 and 4-bit layers), so every wave of a live workgroup has columns.
 template <int WF, bool G1>
 __global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
-    __shared__ __attribute__((aligned(1024))) char As[2 * S_TILE];
+    __shared__ __attribute__((aligned(1024))) char As[3 * S_TILE];  // activation ring, two steps ahead
     const int32_t g = g0 + blockIdx.y;
     int32_t r0, cnt;
     group_rows(a, g, r0, cnt);
@@ -258,31 +258,35 @@ __global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
             }
         };
 
-        // One full step: publish its activations, start the later steps' loads, run its MFMAs.
-        // Weights run two steps ahead in three rotating register sets; per wave the issue order
-        // is A(s+1), W(s+2) during step s, so at the top of step s everything but W(s+1) (the
-        // last WL operations) must have landed.  Past the end the loads repeat the last step
-        // (L2 hits, never consumed) instead of being skipped: with the same load sequence on
-        // every path the compiler's own waits for the weight registers stay exact rather than
-        // falling back to waiting for everything.
+        // One full step: publish its activations, start the loads of step s+2, run its MFMAs.
+        // Activations (three LDS buffers) and weights (three rotating register sets) both run
+        // two steps ahead; per wave the issue order is A(s+2), W(s+2) during step s, so at the
+        // top of step s everything but A(s+1) and W(s+1) (the newest DMA + WL operations; the
+        // DMA only for the waves that copy rows) must have landed.  Past the end the loads
+        // repeat the last step (L2 hits, never consumed) instead of being skipped: with the same
+        // load sequence on every path the compiler's own waits for the weight registers stay
+        // exact rather than falling back to waiting for everything.
         constexpr int WL = NW * (WF == WF_BF16 ? 4 : 3);  // vector-memory operations of one load_full
         auto step = [&](int s, const W (&cur)[NW], W (&nxt2)[NW]) {
-            s_wait_barrier<WL>();
+            if (wave < nrb) s_wait_barrier<4 + WL>();  // wave-uniform; both arms hold one barrier
+            else s_wait_barrier<WL>();
             // the buffer written here was last read in step s-1; past the last step it is not
             // read again in this chunk
-            issue_a(min(s + 1, nsteps - 1), (s + 1) & 1);
+            issue_a(min(s + 2, nsteps - 1), (s + 2) % 3);
             load_full(min(s + 2, nfull - 1), nxt2);
-            compute(std::integral_constant<int, 4>{}, s & 1, cur);
+            compute(std::integral_constant<int, 4>{}, s % 3, cur);
         };
 
-        __syncthreads();  // the previous chunk's reads of both buffers are done
+        __syncthreads();  // the previous chunk's reads of every buffer are done
         W wa[NW], wb[NW], wc[NW];
         issue_a(0, 0);
         if (nfull > 0) {
-            // both prologue loads are unconditional (with one full step the second repeats step 0
-            // and is never used), so the compiler's own wait before the loop's first MFMAs sees
-            // the same load order on entry as around the loop and stays exact
+            // both prologue steps are issued unconditionally (with one full step the second
+            // repeats step 0 and is never used, unless it is the tail's activations), so the
+            // compiler's own wait before the loop's first MFMAs sees the same load order on
+            // entry as around the loop and stays exact
             load_full(0, wa);
+            issue_a(min(1, nsteps - 1), 1);
             load_full(nfull > 1 ? 1 : 0, wb);
             for (int s = 0; s < nfull; s += 3) {  // rotate through three register sets
                 step(s, wa, wc);
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
             W wt[NW];
             load_tail(wt);
             s_wait_all_barrier();
-            compute(std::integral_constant<int, 2>{}, nfull & 1, wt);
+            compute(std::integral_constant<int, 2>{}, nfull % 3, wt);
         }
         // The epilogue reads the accumulators right after the last MFMA, which may sit behind a
         // branch (the 16-row blocks past nrb are skipped).  This compiler's hazard recognizer
