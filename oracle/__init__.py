@@ -28,8 +28,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 
-DT_F32, DT_BF16, DT_Q4 = 0, 1, 2
-_DT = {"f32": DT_F32, "bf16": DT_BF16, "q4": DT_Q4}
+DT_F32, DT_BF16, DT_Q4, DT_FP8 = 0, 1, 2, 3
+_DT = {"f32": DT_F32, "bf16": DT_BF16, "q4": DT_Q4, "fp8": DT_FP8}
 
 
 def build(force: bool = False) -> str:
@@ -75,6 +75,8 @@ def _L():
         lib.oracle_route.argtypes = [p, i64, i32, p, ctypes.POINTER(RouteParams), p, p]
         lib.oracle_route_softmax.restype = ctypes.c_int
         lib.oracle_route_softmax.argtypes = [p, i64, i32, i32, p, p]
+        lib.oracle_e4m3.restype = ctypes.c_double
+        lib.oracle_e4m3.argtypes = [ctypes.c_uint8]
         lib.oracle_swiglu.restype = None
         lib.oracle_swiglu.argtypes = [p, i32, i32, i32] + [p] * 9 + [p]
         lib.oracle_forward.restype = ctypes.c_int
@@ -151,8 +153,16 @@ def route_softmax(logits: np.ndarray, top_k: int):
     return rc, inds, scores
 
 
+def e4m3(codes) -> np.ndarray:
+    """Values (fp64) of OCP E4M3 codes (uint8), one oracle call per code."""
+    c = np.asarray(codes, np.uint8).ravel()
+    f = _L().oracle_e4m3
+    return np.array([f(int(v)) for v in c], np.float64).reshape(np.shape(codes))
+
+
 def swiglu(x: np.ndarray, wg, wu, wd, dtype: str, q4: Optional[dict] = None) -> np.ndarray:
-    """One expert on one row: W_down(silu(W_gate x) * (W_up x)), fp64."""
+    """One expert on one row: W_down(silu(W_gate x) * (W_up x)), fp64.  `q4` holds the
+    quantisation side arrays: q4 scales/offsets ('s_*', 'b_*') or fp8 block scales ('s_*')."""
     x = np.ascontiguousarray(x, np.float64)
     H = x.shape[0]
     I = wg.shape[0]
@@ -204,6 +214,8 @@ def forward(x, router_w, bias, experts: dict, shared: Optional[dict], *, T, H, E
         L.sg, L.bg = c(experts["s_gate"]), c(experts["b_gate"])
         L.su, L.bu = c(experts["s_up"]), c(experts["b_up"])
         L.sd, L.bd = c(experts["s_down"]), c(experts["b_down"])
+    elif expert == "fp8":
+        L.sg, L.su, L.sd = (c(experts[k], np.float32) for k in ("s_gate", "s_up", "s_down"))
     if shared is not None and Is > 0:
         L.swg, L.swu, L.swd = c(shared["gate"]), c(shared["up"]), c(shared["down"])
     L.route_kind = {"deepseek": 0, "softmax": 1}[route_kind]

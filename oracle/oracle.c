@@ -241,14 +241,35 @@ int oracle_route_softmax(const float* logits, int64_t T, int32_t E, int32_t top_
 /* ------------------------------------------------------------------------------------
  * experts
  * ------------------------------------------------------------------------------------ */
-/* element (o, i) of one expert matrix [out, in] in `dtype` (q4: affine group-64 code) */
-static inline double w_at(const void* w, int32_t dtype, const uint16_t* s, const uint16_t* b, int32_t in,
-                          int64_t o, int64_t i) {
+/*
+ * OCP 8-bit floating point, E4M3 ("FN" variant: no infinities): bit 7 sign, bits 6..3 exponent
+ * with bias 7, bits 2..0 mantissa.  Exponent field 0 holds the subnormals m * 2^-9; S.1111.111
+ * is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.  Written from that definition.
+ */
+double oracle_e4m3(uint8_t c) {
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* element (o, i) of one expert matrix [out, in] in `dtype`:
+ *   2 (q4): affine group-64 code, weight = s*q + b (s, b bf16 [out, in/64]);
+ *   3 (fp8): E4M3 code times the fp32 scale of its 128 x 128 block (s fp32
+ *            [ceil(out/128), ceil(in/128)]), the load-time dequantisation of an fp8 checkpoint
+ *            ([Epic56] weight loading: fp8 dequantisation), exact in fp64. */
+static inline double w_at(const void* w, int32_t dtype, const void* s, const void* b, int32_t in, int64_t o,
+                          int64_t i) {
     if (dtype == 2) {
         uint32_t word = ((const uint32_t*)w)[o * (in / 8) + i / 8];
         int q = (int)((word >> (4 * (i % 8))) & 0xFu);
         int64_t g = o * (in / 64) + i / 64;
-        return (double)bf16f(s[g]) * (double)q + (double)bf16f(b[g]);
+        return (double)bf16f(((const uint16_t*)s)[g]) * (double)q + (double)bf16f(((const uint16_t*)b)[g]);
+    }
+    if (dtype == 3) {
+        const int64_t nib = ((int64_t)in + 127) / 128;
+        const double sc = (double)((const float*)s)[(o / 128) * nib + i / 128];
+        return oracle_e4m3(((const uint8_t*)w)[o * (int64_t)in + i]) * sc;
     }
     return (double)act_at(w, dtype, o * (int64_t)in + i);
 }
@@ -258,8 +279,8 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 /* SwiGLU expert: h = silu(x W_gate^T) * (x W_up^T); out = h W_down^T (gate is the first
  * projection and goes through silu; up is linear). */
 void oracle_swiglu(const double* x, int32_t H, int32_t I, int32_t dtype, const void* wg, const void* wu,
-                   const void* wd, const uint16_t* sg, const uint16_t* bg, const uint16_t* su,
-                   const uint16_t* bu, const uint16_t* sd, const uint16_t* bd, double* out) {
+                   const void* wd, const void* sg, const void* bg, const void* su, const void* bu,
+                   const void* sd, const void* bd, double* out) {
     double* h = (double*)malloc(sizeof(double) * (size_t)I);
     for (int32_t n = 0; n < I; ++n) {
         double g = 0.0, u = 0.0;
@@ -277,7 +298,7 @@ void oracle_swiglu(const double* x, int32_t H, int32_t I, int32_t dtype, const v
     free(h);
 }
 
-static size_t expert_elem_bytes(int32_t dtype) { return dtype == 0 ? 4 : 2; }
+static size_t expert_elem_bytes(int32_t dtype) { return dtype == 0 ? 4 : dtype == 3 ? 1 : 2; }
 
 /* pointer to expert e's matrix [out,in] inside a stacked [E,out,in] tensor */
 static const void* expert_mat(const void* base, int32_t dtype, int64_t e, int32_t out, int32_t in) {
@@ -285,8 +306,12 @@ static const void* expert_mat(const void* base, int32_t dtype, int64_t e, int32_
     return (const char*)base + e * (int64_t)out * in * expert_elem_bytes(dtype);
 }
 
-static const uint16_t* expert_sb(const uint16_t* base, int64_t e, int32_t out, int32_t in) {
-    return base ? base + e * (int64_t)out * (in / 64) : NULL;
+/* expert e's scales (or q4 offsets) inside their stacked tensor: q4 bf16 [E,out,in/64], fp8 fp32
+ * [E,ceil(out/128),ceil(in/128)]; NULL stays NULL */
+static const void* expert_sb(const void* base, int32_t dtype, int64_t e, int32_t out, int32_t in) {
+    if (!base) return NULL;
+    if (dtype == 3) return (const float*)base + e * (((int64_t)out + 127) / 128) * (((int64_t)in + 127) / 128);
+    return (const uint16_t*)base + e * (int64_t)out * (in / 64);
 }
 
 /*
@@ -303,9 +328,10 @@ int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, d
     const int32_t H = L->H, E = L->E, I = L->I, Is = L->Is, K = L->route.top_k;
     if (L->T < 0 || n_rows < 0 || H < 1 || I < 1 || Is < 0 || K < 1 || K > E) return -1;
     if (L->act != 0 && L->act != 1) return -1;
-    if (L->expert < 0 || L->expert > 2) return -1;
+    if (L->expert < 0 || L->expert > 3) return -1;
     if (L->expert == 2 && (H % 64 || I % 64 || !L->sg || !L->bg || !L->su || !L->bu || !L->sd || !L->bd))
         return -1;
+    if (L->expert == 3 && (!L->sg || !L->su || !L->sd)) return -1;
     if (Is > 0 && (!L->swg || !L->swu || !L->swd)) return -1;
     if (!rows) n_rows = L->T;
 
@@ -357,9 +383,10 @@ int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, d
                 int64_t e = id[r * K + j];
                 int32_t dt = L->expert;
                 oracle_swiglu(xd, H, I, dt, expert_mat(L->wg, dt, e, I, H), expert_mat(L->wu, dt, e, I, H),
-                              expert_mat(L->wd, dt, e, H, I), expert_sb(L->sg, e, I, H),
-                              expert_sb(L->bg, e, I, H), expert_sb(L->su, e, I, H), expert_sb(L->bu, e, I, H),
-                              expert_sb(L->sd, e, H, I), expert_sb(L->bd, e, H, I), out);
+                              expert_mat(L->wd, dt, e, H, I), expert_sb(L->sg, dt, e, I, H),
+                              expert_sb(L->bg, dt, e, I, H), expert_sb(L->su, dt, e, I, H),
+                              expert_sb(L->bu, dt, e, I, H), expert_sb(L->sd, dt, e, H, I),
+                              expert_sb(L->bd, dt, e, H, I), out);
             } else {
                 oracle_swiglu(xd, H, Is, L->act, L->swg, L->swu, L->swd, NULL, NULL, NULL, NULL, NULL, NULL,
                               out);

@@ -21,7 +21,8 @@
  * oracle_router).  The expert SwiGLU, shared expert and combine are computed in fp64
  * (at least the fp32 accumulation the layer requires).
  *
- * Dtype codes: 0 = fp32, 1 = bf16 (uint16 bit patterns), 2 = 4-bit affine, group 64.
+ * Dtype codes: 0 = fp32, 1 = bf16 (uint16 bit patterns), 2 = 4-bit affine, group 64,
+ * 3 = fp8 E4M3 codes with fp32 scales per 128 x 128 block.
  */
 #ifndef DSMOE_ORACLE_H
 #define DSMOE_ORACLE_H
@@ -43,7 +44,7 @@ typedef struct oracle_layer {
     int64_t T;
     int32_t H, E, I, Is; /* Is == 0: no shared expert */
     int32_t act;         /* 0 fp32, 1 bf16: x, router, shared weights */
-    int32_t expert;      /* 0 fp32, 1 bf16, 2 q4g64: routed expert weights */
+    int32_t expert;      /* 0 fp32, 1 bf16, 2 q4g64, 3 fp8 block-scaled: routed expert weights */
     oracle_route_params route;
     const void* x;        /* [T,H] act */
     const void* router;   /* [E,H] act */
@@ -51,8 +52,10 @@ typedef struct oracle_layer {
     const float* offset;  /* NULL or [E]: added to the router logits */
     const void* wg;       /* [E,I,H] (q4: uint32 [E,I,H/8]) */
     const void* wu;       /* [E,I,H] */
-    const void* wd;       /* [E,H,I] (q4: uint32 [E,H,I/8]) */
-    const uint16_t *sg, *bg, *su, *bu, *sd, *bd; /* q4 only: bf16 scale / offset [E,out,in/64] */
+    const void* wd;       /* [E,H,I] (q4: uint32 [E,H,I/8]; fp8: uint8 [E,H,I]) */
+    /* q4: bf16 scale s* / offset b* [E,out,in/64]; fp8: fp32 scales s* [E,ceil(out/128),ceil(in/128)],
+     * b* unused */
+    const void *sg, *bg, *su, *bu, *sd, *bd;
     const void* swg;      /* [Is,H] act */
     const void* swu;      /* [Is,H] act */
     const void* swd;      /* [H,Is] act */
@@ -76,11 +79,14 @@ int oracle_route(const float* logits, int64_t T, int32_t E, const float* bias, c
 /* Softmax gate over T rows (see oracle.c for the reading taken).  Returns 0, or -1 on
  * invalid arguments (outputs untouched). */
 int oracle_route_softmax(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* inds, float* scores);
+/* Value of one OCP E4M3 code (NaN for S.1111.111), exact. */
+double oracle_e4m3(uint8_t c);
 /* SwiGLU expert on one fp64 input row: out[H] = W_down (silu(W_gate x) * (W_up x)).
- * w* point at ONE expert's matrices in `dtype`; s*, b* are its q4 scale/offset (or NULL). */
+ * w* point at ONE expert's matrices in `dtype`; s*, b* are its q4 scale/offset or fp8 block
+ * scales (or NULL). */
 void oracle_swiglu(const double* x, int32_t H, int32_t I, int32_t dtype, const void* wg, const void* wu,
-                   const void* wd, const uint16_t* sg, const uint16_t* bg, const uint16_t* su,
-                   const uint16_t* bu, const uint16_t* sd, const uint16_t* bd, double* out);
+                   const void* wd, const void* sg, const void* bg, const void* su, const void* bu,
+                   const void* sd, const void* bd, double* out);
 
 /* Whole layer for the tokens rows[0..n_rows) (rows == NULL: all T tokens in order).
  * y: fp64 [n_rows,H]; inds/scores: [n_rows,K] (may be NULL); logits: [n_rows,E] (may be NULL).

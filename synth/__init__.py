@@ -11,7 +11,9 @@ Storage conventions (numpy):
   * bf16 tensors are ``uint16`` arrays holding the bf16 bit patterns;
   * 4-bit packed expert weights are ``uint32`` arrays ``[..., out, in/8]``
     (element i of a row at bits ``4*(i%8)`` of word ``i//8``) with bf16
-    scale and offset arrays ``[..., out, in/64]``.
+    scale and offset arrays ``[..., out, in/64]``;
+  * fp8 expert weights are ``uint8`` OCP E4M3 codes ``[..., out, in]`` with
+    fp32 scales ``[..., ceil(out/128), ceil(in/128)]`` (one per 128 x 128 block).
 Weight layout is "expert stacking": ``[E, out, in]`` with the input axis
 contiguous; the router is ``[E, H]``; shared weights are ``[Is, H]``,
 ``[Is, H]``, ``[H, Is]``.
@@ -60,6 +62,7 @@ def _L():
         lib.synth_normal_bf16.argtypes = [u64, u64, u64, i64, d, d, p]
         lib.synth_f32_to_bf16.argtypes = [p, i64, p]
         lib.synth_q4_normal.argtypes = [u64, u64, u64, i64, i64, d, p, p, p]
+        lib.synth_fp8_normal.argtypes = [u64, u64, u64, i64, i64, i64, d, p, p]
         lib.synth_uniform_f64.argtypes = [u64, u64, u64, i64, p]
         _lib = lib
     return _lib
@@ -113,6 +116,17 @@ def q4_normal(seed, tid, rows, cols, std, start=0):
     return q, s, b
 
 
+def fp8_normal(seed, tid, nmat, rows, cols, std, start=0):
+    """fp8 (OCP E4M3) quantisation of normal draws with one fp32 scale per 128 x 128 block of
+    each of `nmat` stacked [rows, cols] matrices: (codes uint8 [nmat, rows, cols], scales fp32
+    [nmat, ceil(rows/128), ceil(cols/128)])."""
+    assert cols % 2 == 0 and start % 2 == 0
+    q = np.empty((nmat, rows, cols), np.uint8)
+    s = np.empty((nmat, (rows + 127) // 128, (cols + 127) // 128), np.float32)
+    _L().synth_fp8_normal(seed, tid, start, nmat, rows, cols, std, _ptr(q), _ptr(s))
+    return q, s
+
+
 def permutation(seed: int, tid: int, n: int) -> np.ndarray:
     """Seeded Fisher-Yates permutation of 0..n-1 (uniform draws from the same generator)."""
     p = np.arange(n, dtype=np.int64)
@@ -137,7 +151,7 @@ class Workload:
     I: int
     Is: int
     act: str        # "f32" | "bf16"
-    expert: str     # "f32" | "bf16" | "q4"
+    expert: str     # "f32" | "bf16" | "q4" | "fp8"
     bias_std: float
     norm: bool
     rsf: float
@@ -248,7 +262,8 @@ def gen_x(w: Workload, router: Optional[np.ndarray] = None, bias: Optional[np.nd
 
 def gen_expert_weights(w: Workload, e0: int = 0, e1: Optional[int] = None) -> dict:
     """Routed expert weights for experts [e0, e1): gate/up [n, I, H], down [n, H, I].
-    For expert dtype q4 returns packed uint32 codes plus bf16 scale ('s_*') and offset ('b_*')."""
+    For expert dtype q4 returns packed uint32 codes plus bf16 scale ('s_*') and offset ('b_*');
+    for fp8, uint8 E4M3 codes plus fp32 scales per 128 x 128 block ('s_*')."""
     e1 = w.E if e1 is None else e1
     n = e1 - e0
     sg, sd = 1.0 / math.sqrt(w.H), 1.0 / math.sqrt(w.I)
@@ -256,7 +271,9 @@ def gen_expert_weights(w: Workload, e0: int = 0, e1: Optional[int] = None) -> di
     for nm, tid, o, i, std in (("gate", TID_WG, w.I, w.H, sg), ("up", TID_WU, w.I, w.H, sg),
                                ("down", TID_WD, w.H, w.I, sd)):
         start = e0 * o * i
-        if w.expert == "q4":
+        if w.expert == "fp8":
+            out[nm], out["s_" + nm] = fp8_normal(w.wseed, tid, n, o, i, std, start=start)
+        elif w.expert == "q4":
             q, s, b = q4_normal(w.wseed, tid, n * o, i, std, start=start)
             out[nm] = q.reshape(n, o, i // 8)
             out["s_" + nm] = s.reshape(n, o, i // 64)
@@ -291,6 +308,9 @@ def expert_bytes(w: Workload) -> int:
     n = 3 * w.I * w.H
     if w.expert == "q4":
         return n // 2 + 2 * 2 * (n // 64)
+    if w.expert == "fp8":
+        nb = 2 * (-(-w.I // 128)) * (-(-w.H // 128)) + (-(-w.H // 128)) * (-(-w.I // 128))
+        return n + 4 * nb
     return n * (4 if w.expert == "f32" else 2)
 
 

@@ -160,6 +160,61 @@ void synth_q4_normal(uint64_t seed, uint64_t tid, uint64_t start, int64_t rows, 
     }
 }
 
+/* fp32 -> OCP E4M3 code, round to nearest even, magnitudes above 448 saturate to 448 (the
+ * quantiser of an fp8 checkpoint; never produces NaN) */
+static uint8_t e4m3_encode(float v) {
+    uint8_t sg = signbit(v) ? 0x80 : 0x00;
+    float a = fabsf(v);
+    if (!(a < 448.0f)) return (uint8_t)(sg | 0x7E);
+    if (a < 0x1p-6f) {                       /* subnormal range: steps of 2^-9 */
+        int m = (int)rintf(a * 512.0f);      /* exact scaling, RNE; m == 8 is the smallest normal */
+        return (uint8_t)(sg | m);
+    }
+    int ex;
+    frexpf(a, &ex);                          /* a = f * 2^ex, f in [0.5, 1) */
+    int E = ex - 1;                          /* a in [2^E, 2^(E+1)) */
+    int m = (int)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);
+    if (m == 8) { m = 0; E += 1; }
+    int e = E + 7;
+    if (e > 15 || (e == 15 && m == 7)) return (uint8_t)(sg | 0x7E);
+    return (uint8_t)(sg | (e << 3) | m);
+}
+
+/*
+ * fp8 (E4M3) quantisation with one fp32 scale per 128 x 128 block, of `nmat` stacked [rows, cols]
+ * matrices whose fp32 values are the normals of tensor (seed, tid) from element `start`, scaled
+ * by std (cols even).  Block scale = max |w| / 448 (1 for an all-zero block); code = E4M3 of
+ * w / scale.  q: uint8 [nmat, rows, cols]; s: fp32 [nmat, ceil(rows/128), ceil(cols/128)].
+ */
+void synth_fp8_normal(uint64_t seed, uint64_t tid, uint64_t start, int64_t nmat, int64_t rows, int64_t cols,
+                      double std, uint8_t* q, float* s) {
+    uint64_t key = key_of(seed, tid);
+    const int64_t nbr = (rows + 127) / 128, nbc = (cols + 127) / 128;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t blk = 0; blk < nmat * nbr * nbc; ++blk) {
+        const int64_t mt = blk / (nbr * nbc), br = (blk / nbc) % nbr, bc = blk % nbc;
+        const int64_t r0 = br * 128, c0 = bc * 128;
+        const int64_t nr = rows - r0 < 128 ? rows - r0 : 128, nc = cols - c0 < 128 ? cols - c0 : 128;
+        float w[128 * 128];
+        float amax = 0.0f;
+        for (int64_t r = 0; r < nr; ++r)
+            for (int64_t c = 0; c < nc; c += 2) {
+                const uint64_t el = start + (uint64_t)((mt * rows + r0 + r) * cols + c0 + c);
+                double z0, z1; /* el is even: elements el, el+1 form one pair */
+                normal_pair(key, el >> 1, &z0, &z1);
+                w[r * 128 + c] = (float)(std * z0);
+                w[r * 128 + c + 1] = (float)(std * z1);
+                if (fabsf(w[r * 128 + c]) > amax) amax = fabsf(w[r * 128 + c]);
+                if (fabsf(w[r * 128 + c + 1]) > amax) amax = fabsf(w[r * 128 + c + 1]);
+            }
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        for (int64_t r = 0; r < nr; ++r)
+            for (int64_t c = 0; c < nc; ++c)
+                q[(mt * rows + r0 + r) * cols + c0 + c] = e4m3_encode(w[r * 128 + c] / sc);
+        s[(mt * nbr + br) * nbc + bc] = sc;
+    }
+}
+
 /* out[j] = uniform [0,1) double from the 53 high bits of counter start+j */
 void synth_uniform_f64(uint64_t seed, uint64_t tid, uint64_t start, int64_t n, double* out) {
     uint64_t key = key_of(seed, tid);
