@@ -106,6 +106,11 @@ def layer_flops(w) -> float:
     return 2.0 * w.T * w.H * w.E + 6.0 * w.H * w.I * w.T * w.K + 6.0 * w.H * w.Is * w.T
 
 
+def synth_T(name: str) -> int:
+    import synth
+    return synth.WORKLOADS[name].T
+
+
 def run_workload(name: str, steps: int, warmup: int, cache: dict):
     import numpy as np
     import torch
@@ -259,8 +264,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "dense"],
-                    help="c3: DSV3 prefill (headline); c2: decode; c4: 4-bit experts; dense: DSV3 dense MLP layer")
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5", "c6", "dense"],
+                    help="c3: DSV3 prefill (headline); c2: decode; c4: 4-bit experts; c5 / c6: fp8 experts, "
+                         "prefill / decode; dense: DSV3 dense MLP layer")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode batch")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     args = ap.parse_args()
@@ -291,8 +297,9 @@ def main():
     w = main_res["w"]
     sec = None
     if not args.no_secondary:
-        other = "c3" if args.workload == "c2" else "c2"
-        sec = run_workload(other, max(args.steps, 20) if other == "c2" else args.steps, args.warmup, cache)
+        other = {"c2": "c3", "c5": "c6", "c6": "c5"}.get(args.workload, "c2")
+        small = synth_T(other) <= 256
+        sec = run_workload(other, max(args.steps, 20) if small else args.steps, args.warmup, cache)
 
     def summary(res):
         wl = res["w"]
@@ -302,7 +309,7 @@ def main():
             ach = gemm1_bytes(wl, res["n_hit"]) / (res["gemm1_ms"] / 1e3) / 1e9
             roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                     "traffic": TRAFFIC_GB.get(wl.name), "traffic_unit": "GB per launch",
-                    "kernel": "stream_gemm<bf16, gate/up> (weight-streaming gate/up + SwiGLU)"}
+                    "kernel": f"stream_gemm<{wl.expert}, gate/up> (weight-streaming gate/up + SwiGLU)"}
             layer = layer_bytes(wl, res["n_hit"]) / (res["step_ms"] / 1e3) / 1e9
             roof["layer_achieved"] = layer
             roof["layer_frac"] = layer / PEAK_HBM_GBS
@@ -313,8 +320,8 @@ def main():
                     "traffic_unit": "GB per launch",
                     "kernel": ("gemm_dma<256, true> (tiled gate/up + SwiGLU: groups above 64 rows and the "
                                "shared expert)") if wl.expert == "bf16" else
-                              ("tiled gate/up + SwiGLU kernels: gemm_tiled<BM, true, q4> for the 4-bit routed "
-                               "groups above 64 rows, gemm_dma<BM, true> for the bf16 shared expert")}
+                              (f"tiled gate/up + SwiGLU kernels: gemm_dma_wq<{wl.expert}, true> for the {wl.expert} "
+                               "routed groups above 64 rows, gemm_dma<128, true> for the bf16 shared expert")}
             layer = layer_flops(wl) / (res["step_ms"] / 1e3) / 1e12
             roof["layer_achieved"] = layer
             roof["layer_frac"] = layer / PEAK_BF16_TFLOPS

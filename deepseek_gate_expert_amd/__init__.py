@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_HIP, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_Q4G64 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_Q4G64, MOE_FP8 = 0, 1, 2, 3
 MOE_MAX_EXPERTS, MOE_MAX_TOP_K = 1024, 64
 MOE_ROUTE_DEEPSEEK, MOE_ROUTE_SOFTMAX = 0, 1
 MOE_STAGE_ROUTER, MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = range(6)
@@ -229,7 +229,8 @@ def moe_forward_workspace_size(desc: LayerDesc) -> int:
 def moe_forward(desc: LayerDesc, x, router_w, bias, experts: dict, shared: Optional[dict], y, logit_offset=None,
                 inds_out=None, scores_out=None, workspace=None, stream=None) -> int:
     """Whole MoE layer forward (see dsmoe.h).  experts: dict with 'gate', 'up', 'down' (and for
-    4-bit weights 's_gate', 'b_gate', 's_up', 'b_up', 's_down', 'b_down'); shared: dict with
+    4-bit weights 's_gate', 'b_gate', 's_up', 'b_up', 's_down', 'b_down'; for fp8 weights the
+    fp32 block scales 's_gate', 's_up', 's_down'); shared: dict with
     'gate', 'up', 'down' (and optionally 'sgate', the [H] gate vector) or None.  bias may be
     None with the softmax gate."""
     import torch

@@ -48,8 +48,8 @@ struct TilePlan {
 };
 
 // Shapes-only decision (no device reads): tiles of 256 rows when the average group is large
-// (bf16 weights only: the 4-bit kernel keeps its dequantised operands in registers and runs
-// 128-row tiles).
+// (bf16 weights only: the 4-bit and fp8 kernel keeps its dequantised operands in registers and
+// runs 128-row tiles).
 TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     TilePlan p{false, 128, 0};
     if (d->act_dtype != MOE_BF16 || d->T <= STREAM_MAX_ROWS) return p;
@@ -111,7 +111,8 @@ int check_desc(const moe_layer_desc* d) {
     if (!d) return MOE_ERR_INVALID;
     if (d->T < 0 || d->H < 1 || d->E < 1 || d->I < 1 || d->I_shared < 0) return MOE_ERR_INVALID;
     const int32_t a = d->act_dtype, w = d->expert_dtype;
-    const bool combo = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_Q4G64));
+    const bool combo =
+        (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && (w == MOE_BF16 || w == MOE_Q4G64 || w == MOE_FP8));
     if (!combo) return MOE_ERR_INVALID;
     if (d->route_kind != MOE_ROUTE_DEEPSEEK && d->route_kind != MOE_ROUTE_SOFTMAX) return MOE_ERR_INVALID;
     int rc = MOE_OK;
@@ -352,6 +353,9 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
         (!ptr_ok(ew->s_gate, false) || !ptr_ok(ew->b_gate, false) || !ptr_ok(ew->s_up, false) ||
          !ptr_ok(ew->b_up, false) || !ptr_ok(ew->s_down, false) || !ptr_ok(ew->b_down, false)))
         return MOE_ERR_INVALID;
+    if (d->expert_dtype == MOE_FP8 &&
+        (!ptr_ok(ew->s_gate, false) || !ptr_ok(ew->s_up, false) || !ptr_ok(ew->s_down, false)))
+        return MOE_ERR_INVALID;
     if (d->I_shared > 0) {
         if (!sw || !ptr_ok(sw->w_gate, false) || !ptr_ok(sw->w_up, false) || !ptr_ok(sw->w_down, false) ||
             !ptr_ok(sw->w_sgate, true))
@@ -419,6 +423,10 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
         a.bu = (const bf16_t*)ew->b_up;
         a.sd = (const bf16_t*)ew->s_down;
         a.bd = (const bf16_t*)ew->b_down;
+    } else if (d->expert_dtype == MOE_FP8) {
+        a.fsg = (const float*)ew->s_gate;
+        a.fsu = (const float*)ew->s_up;
+        a.fsd = (const float*)ew->s_down;
     }
     if (d->I_shared > 0) {
         a.swg = sw->w_gate;
@@ -428,15 +436,16 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
 
     const int32_t E = d->E;
     const int32_t gend = E + (d->I_shared > 0 ? 1 : 0);
-    const bool f32 = d->act_dtype == MOE_F32, q4 = d->expert_dtype == MOE_Q4G64;
+    const bool f32 = d->act_dtype == MOE_F32;
+    const bool quant = d->expert_dtype == MOE_Q4G64 || d->expert_dtype == MOE_FP8;
     TilePlan tp{false, 128, 0};
     if (!f32) {
         const int ts = tiled_state();
         if (ts != 3) tp = plan_tiles(d, ts == 1);
     }
     a.stream_max_rows = tp.on ? STREAM_MAX_ROWS : 0x7fffffff;
-    const int32_t rdt = q4 ? MOE_Q4G64 : MOE_BF16;
-    const int32_t split = q4 ? E : gend;  // 4-bit routed groups vs bf16 (shared) group
+    const int32_t rdt = quant ? d->expert_dtype : MOE_BF16;
+    const int32_t split = quant ? E : gend;  // quantised routed groups vs the bf16 (shared) group
     // weight-streaming kernels of one expert-GEMM pass (groups of at most stream_max_rows rows)
     auto streamed = [&](bool first) -> int {
         if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));

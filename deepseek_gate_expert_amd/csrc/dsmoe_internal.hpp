@@ -47,8 +47,11 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(bf16_t, b);
 }
 
+// two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // One launch of the grouped expert GEMMs.  Groups g in [0, E) are the routed experts with
@@ -65,10 +68,11 @@ struct GroupedArgs {
     const void* x;               // [T, H] act
     void* h;                     // [TK + T, ldh] act (SwiGLU intermediate)
     void* o;                     // [TK + T, H] act (per-row expert output)
-    const void* wg;              // routed [E, I, H] (q4: uint32 [E, I, H/8])
+    const void* wg;              // routed [E, I, H] (q4: uint32 [E, I, H/8]; fp8: uint8 codes)
     const void* wu;
     const void* wd;              // routed [E, H, I]
     const bf16_t *sg, *bg, *su, *bu, *sd, *bd;  // q4 scale / offset [E, out, in/64]
+    const float *fsg, *fsu, *fsd;  // fp8 block scales [E, ceil(out/128), ceil(in/128)]
     const void* swg;             // shared [Is, H] act
     const void* swu;
     const void* swd;             // shared [H, Is] act
@@ -84,7 +88,7 @@ int32_t dispatch_blocks(int64_t TK);
 hipError_t launch_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_slot, int32_t* slot_row, int32_t* blk, hipStream_t s);
 // bf16-activation expert GEMMs for groups [g0, g1); wdt = weight dtype of those groups
-// (MOE_BF16 or MOE_Q4G64; the shared group E is always bf16)
+// (MOE_BF16, MOE_Q4G64 or MOE_FP8; the shared group E is always bf16)
 hipError_t launch_gemm1_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s);
 hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s);
 // fp32 layers: all routed rows and the shared rows in one launch each

@@ -25,24 +25,44 @@
 //
 // 4-bit weights (affine, groups of 64 along the input axis): each lane loads the 16 bytes of
 // codes covering its 32 k values plus that group's bf16 scale and offset, and forms
-// bf16(s*q + b) in registers before the MFMA.
+// bf16(s*q + b) in registers before the MFMA.  fp8 weights (OCP E4M3 codes, one fp32 scale per
+// 128 x 128 block): each lane loads the 32 code bytes of its 32 k values plus the block's scale,
+// and forms bf16(value * scale) in registers (hardware E4M3 -> fp32 conversion, fp32 multiply,
+// round to nearest even).
 #include "dsmoe_internal.hpp"
 
 namespace dsmoe {
 namespace {
 
-enum { WF_BF16 = 0, WF_Q4 = 1 };
+enum { WF_BF16 = 0, WF_Q4 = 1, WF_F8 = 2 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float b) {
     u32x4 r;
+    // codes 2j and 2j+1 are the low and high nibble of byte j: split the nibbles into bytes once,
+    // then convert each byte directly (v_cvt_f32_ubyte{0..3})
+    const uint32_t lo4 = w & 0x0F0F0F0Fu, hi4 = (w >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float lo = __builtin_fmaf(s, (float)((w >> (8 * j)) & 0xFu), b);
-        const float hi = __builtin_fmaf(s, (float)((w >> (8 * j + 4)) & 0xFu), b);
+        const float lo = __builtin_fmaf(s, (float)((lo4 >> (8 * j)) & 0xFFu), b);
+        const float hi = __builtin_fmaf(s, (float)((hi4 >> (8 * j)) & 0xFFu), b);
         r[j] = pack_bf16x2(lo, hi);
     }
+    return as_bf16x8(r);
+}
+
+// eight E4M3 codes (two words, code i at bits 8*(i%4) of word i/4) -> bf16(value * s)
+__device__ __forceinline__ bf16x8 dequant_f8x8(uint32_t lo, uint32_t hi, float s) {
+    u32x4 r;
+    const auto v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);  // codes 0, 1
+    const auto v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);   // codes 2, 3
+    const auto v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const auto v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    r[0] = pack_bf16x2(v0[0] * s, v0[1] * s);
+    r[1] = pack_bf16x2(v1[0] * s, v1[1] * s);
+    r[2] = pack_bf16x2(v2[0] * s, v2[1] * s);
+    r[3] = pack_bf16x2(v3[0] * s, v3[1] * s);
     return as_bf16x8(r);
 }
 
@@ -52,6 +72,8 @@ struct WRow {
     const uint32_t* q; // packed codes row (WF_Q4)
     const bf16_t* s;   // scale row (WF_Q4)
     const bf16_t* b;   // offset row (WF_Q4)
+    const uint8_t* c8; // E4M3 codes row (WF_F8)
+    const float* fs;   // block scales of the row's 128-row block, one per 128 k (WF_F8)
 };
 
 // k layout of one reduction step inside a wave.  Lane l (group q = l / 16) supplies, for the
@@ -59,7 +81,7 @@ struct WRow {
 // so the 4 lanes of a row read 64 contiguous bytes per load instruction; 4-bit rows: kq = 32 q,
 // PS = 8, so a lane's codes for a step are one 16-byte word group.  A and B use the same layout.
 template <int WF>
-struct KLayout {
+struct KLayout {  // 4-bit and fp8 rows share one layout
     static constexpr int PS = WF == WF_BF16 ? 32 : 8;
     static __device__ __forceinline__ int kq(int lane, int np) { return (lane >> 4) * (WF == WF_BF16 ? 8 : 8 * np); }
 };
@@ -82,14 +104,27 @@ struct WRegs<WF_Q4> {
     bf16_t s, b;
     __device__ __forceinline__ bf16x8 frag(int i) const { return dequant8(q[i], bf16_to_f32(s), bf16_to_f32(b)); }
 };
+template <>
+struct WRegs<WF_F8> {
+    u32x4 q[2];  // 32 codes; piece i is words 2(i%2), 2(i%2)+1 of q[i/2]
+    float s;
+    __device__ __forceinline__ bf16x8 frag(int i) const {
+        return dequant_f8x8(q[i >> 1][2 * (i & 1)], q[i >> 1][2 * (i & 1) + 1], s);
+    }
+};
 
 // NP pieces of 8 k values (see KLayout) starting at k.  Vector-memory operations issued: NP
-// 16-byte loads (bf16), or codes + scale + offset = 3 (4-bit).
+// 16-byte loads (bf16), codes + scale + offset = 3 (4-bit), or NP/2 16-byte code loads + scale
+// (fp8: 3 for a full step).
 template <int WF, int NP>
 __device__ __forceinline__ void load_w(const WRow& r, int k, WRegs<WF>& out) {
     if constexpr (WF == WF_BF16) {
 #pragma unroll
         for (int i = 0; i < NP; ++i) out.v[i] = as_bf16x8(*(const u32x4*)(r.w + k + i * KLayout<WF>::PS));
+    } else if constexpr (WF == WF_F8) {
+        out.s = r.fs[k >> 7];
+#pragma unroll
+        for (int i = 0; i < NP / 2; ++i) out.q[i] = *(const u32x4*)(r.c8 + k + 16 * i);
     } else {
         out.s = r.s[k >> 6];
         out.b = r.b[k >> 6];
@@ -123,7 +158,7 @@ template <int WF>
 __device__ __forceinline__ WRow weight_row(const GroupedArgs& a, int sel, int32_t g, bool shared, int32_t n,
                                            int32_t out_dim, int32_t in_dim) {
     // sel: 0 gate, 1 up, 2 down
-    WRow r = {nullptr, nullptr, nullptr, nullptr};
+    WRow r = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
     if (shared) {
         const bf16_t* base = (const bf16_t*)(sel == 0 ? a.swg : sel == 1 ? a.swu : a.swd);
         r.w = base + (int64_t)n * in_dim;
@@ -133,6 +168,10 @@ __device__ __forceinline__ WRow weight_row(const GroupedArgs& a, int sel, int32_
     if constexpr (WF == WF_BF16) {
         const bf16_t* base = (const bf16_t*)(sel == 0 ? a.wg : sel == 1 ? a.wu : a.wd);
         r.w = base + row * in_dim;
+    } else if constexpr (WF == WF_F8) {
+        r.c8 = (const uint8_t*)(sel == 0 ? a.wg : sel == 1 ? a.wu : a.wd) + row * in_dim;
+        const int64_t nbo = (out_dim + 127) / 128, nbi = (in_dim + 127) / 128;
+        r.fs = (sel == 0 ? a.fsg : sel == 1 ? a.fsu : a.fsd) + ((int64_t)g * nbo + n / 128) * nbi;
     } else {
         const uint32_t* base = (const uint32_t*)(sel == 0 ? a.wg : sel == 1 ? a.wu : a.wd);
         r.q = base + row * (in_dim / 8);
@@ -335,7 +374,9 @@ hipError_t launch_gemm1_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32
     if (g1 <= g0) return hipSuccess;
     const int32_t N = max(a.I, a.Is);
     const dim3 grid((N + 63) / 64, g1 - g0);
-    if (wdt == MOE_Q4G64)
+    if (wdt == MOE_FP8)
+        hipLaunchKernelGGL((stream_gemm<WF_F8, true>), grid, dim3(256), 0, s, a, g0);
+    else if (wdt == MOE_Q4G64)
         hipLaunchKernelGGL((stream_gemm<WF_Q4, true>), grid, dim3(256), 0, s, a, g0);
     else
         hipLaunchKernelGGL((stream_gemm<WF_BF16, true>), grid, dim3(256), 0, s, a, g0);
@@ -345,7 +386,9 @@ hipError_t launch_gemm1_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32
 hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s) {
     if (g1 <= g0) return hipSuccess;
     const dim3 grid((a.H + 63) / 64, g1 - g0);
-    if (wdt == MOE_Q4G64)
+    if (wdt == MOE_FP8)
+        hipLaunchKernelGGL((stream_gemm<WF_F8, false>), grid, dim3(256), 0, s, a, g0);
+    else if (wdt == MOE_Q4G64)
         hipLaunchKernelGGL((stream_gemm<WF_Q4, false>), grid, dim3(256), 0, s, a, g0);
     else
         hipLaunchKernelGGL((stream_gemm<WF_BF16, false>), grid, dim3(256), 0, s, a, g0);

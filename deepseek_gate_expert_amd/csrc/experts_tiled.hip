@@ -9,8 +9,8 @@
 //     weights -- for GEMM-1 the gate and up rows of the same 128 output columns, for GEMM-2 256
 //     rows of W_down -- with v_mfma_f32_32x32x16_bf16 and fp32 accumulators;
 //   * operands reach LDS by direct-to-LDS DMA in k-stages of 64 (one 128-byte line per row),
-//     through a ring of stages, with one barrier per stage (gemm_dma); 4-bit weights skip LDS and
-//     are dequantised in registers (gemm_dma_q4);
+//     through a ring of stages, with one barrier per stage (gemm_dma); 4-bit and fp8 weights skip
+//     LDS and are dequantised in registers (gemm_dma_wq);
 //   * the list of (group, first row) tiles is built on the device from the dispatch offsets, so
 //     no count ever returns to the host; the grid is an upper bound and surplus workgroups exit;
 //   * workgroup ids are remapped so that the workgroups an XCD receives (ids congruent mod 8)
@@ -32,12 +32,30 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float b) {
     u32x4 r;
+    // codes 2j and 2j+1 are the low and high nibble of byte j: split the nibbles into bytes once,
+    // then convert each byte directly (v_cvt_f32_ubyte{0..3})
+    const uint32_t lo4 = w & 0x0F0F0F0Fu, hi4 = (w >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float lo = __builtin_fmaf(s, (float)((w >> (8 * j)) & 0xFu), b);
-        const float hi = __builtin_fmaf(s, (float)((w >> (8 * j + 4)) & 0xFu), b);
+        const float lo = __builtin_fmaf(s, (float)((lo4 >> (8 * j)) & 0xFFu), b);
+        const float hi = __builtin_fmaf(s, (float)((hi4 >> (8 * j)) & 0xFFu), b);
         r[j] = pack_bf16x2(lo, hi);
     }
+    return r;
+}
+
+// eight E4M3 codes (two words, code i at bits 8*(i%4) of word i/4) -> bf16(value * s): hardware
+// E4M3 -> fp32 conversion, fp32 multiply, round to nearest even
+__device__ __forceinline__ u32x4 dequant_f8x8(uint32_t lo, uint32_t hi, float s) {
+    u32x4 r;
+    const auto v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);  // codes 0, 1
+    const auto v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);   // codes 2, 3
+    const auto v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+    const auto v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    r[0] = pack_bf16x2(v0[0] * s, v0[1] * s);
+    r[1] = pack_bf16x2(v1[0] * s, v1[1] * s);
+    r[2] = pack_bf16x2(v2[0] * s, v2[1] * s);
+    r[3] = pack_bf16x2(v3[0] * s, v3[1] * s);
     return r;
 }
 
@@ -316,36 +334,83 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
 
 
 // ---------------------------------------------------------------------------------------------
-// 4-bit weights (affine, groups of 64 along the reduction axis), tiles of 128 rows.  Same tile
-// shape, activation ring and tile list as gemm_dma; the packed codes are four times smaller than
-// bf16 rows, so they skip LDS: each lane loads the codes it multiplies straight into registers,
-// two stages ahead, with its row's scale and offset for the stage (one 64-k stage is one
-// quantisation group), and forms bf16(s*q + b) one k16 step before the MFMAs that consume it.
-// The dequantisation runs on the vector ALU beside the matrix cores; to keep it at one pass per
-// weight the four waves split the tile by columns (1 x 4): wave w owns all 128 rows and, for
-// GEMM-1, the gate and up rows of output columns [32 w, 32 w + 32), for GEMM-2 the 64 columns
-// [64 w, 64 w + 64).  Within a stage the k chunks are taken in the order 4h + s (lane half h,
-// step s) for both operands, so a lane's codes for the whole stage are one 16-byte load.
-// Per wave and stage the vector-memory issue order is: codes/scales of stage kt+2, then the
-// activation DMA of stage kt+NQ (A_DMA loads).  At the barrier before the last step of stage
-// kt everything but the newest A_DMA operations must have landed: that covers the activations
-// and the codes of stage kt+1.
+// Quantised weights, tiles of 128 rows: 4-bit (affine, groups of 64 along the reduction axis)
+// or fp8 (OCP E4M3 codes, one fp32 scale per 128 x 128 block).  Same tile shape and tile list
+// as gemm_dma.  Every operand of a 64-k stage -- the activation rows, the weight codes and the
+// scales (and 4-bit offsets) -- enters LDS by DMA, in a ring of three stages (stages kt+1 and
+// kt+2 in flight while kt is computed).  With no register loads in the loop the compiler inserts
+// no waits of its own: the only waits are the explicit count + barrier per stage.  (Loading the
+// codes into registers beside an LDS DMA ring made the compiler wait for every outstanding load
+// before each use of them, which exposed the full memory latency once per stage.)
+// The dequantisation -- bf16(s*q + b), resp. bf16(value * scale) -- runs on the vector ALU
+// beside the matrix cores, one k16 step ahead of the MFMAs that consume it; to keep it at one
+// pass per weight the four waves split the tile by columns (1 x 4): wave w owns all 128 rows
+// and, for GEMM-1, the gate and up rows of output columns [32 w, 32 w + 32), for GEMM-2 the 64
+// columns [64 w, 64 w + 64).  Wave w also fetches those 64 weight rows' codes and scales.
+// Within a stage the k chunks are taken in the order 4h + s (lane half h, step s) for both
+// operands, so a lane's codes for the whole stage are one (4-bit) or two (fp8) 16-byte chunks.
+//
+// LDS layout of one stage slot:
+//   activations  BM rows x 128 bytes, chunk swizzle dma::swz (as gemm_dma)
+//   codes        256 weight rows x CB bytes (CB = 32 for 4-bit, 64 for fp8); weight row
+//                rho = 64 w + 32 j + i is column i of wave w's block j; 16-byte chunk c of
+//                row rho sits at chunk c ^ cswz(rho), which keeps each phase of the lanes' reads
+//                (consecutive rows, one chunk each) spread over all banks
+//   side data    fp8: one fp32 scale per weight row (4 * 256 bytes); 4-bit: the aligned 32-bit
+//                word holding the row's bf16 scale for the stage, then the one holding its
+//                offset (2 * 4 * 256 bytes); the bf16 half is picked by the element's parity
 // ---------------------------------------------------------------------------------------------
-namespace q4t {
-constexpr int BM = 128;
-constexpr int NQ = 3;  // activation ring depth
-constexpr int ring_bytes() { return NQ * BM * dma::ROWB; }
-}  // namespace q4t
+enum { WQ_Q4 = 0, WQ_F8 = 1 };
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
+namespace wq {
+constexpr int BM = 128;
+constexpr int NS = 3;                          // ring depth
+constexpr int A_BYTES = BM * dma::ROWB;        // activations of one stage
+template <int WQ>
+struct Fmt {
+    static constexpr int CB = WQ == WQ_F8 ? 64 : 32;            // code bytes per weight row per stage
+    static constexpr int ROWS_PER_DMA = 1024 / CB;              // weight rows per DMA instruction
+    static constexpr int C_DMA = 64 / ROWS_PER_DMA;             // code DMAs per wave per stage
+    static constexpr int S_DMA = WQ == WQ_F8 ? 1 : 2;           // side-data DMAs per wave per stage
+    static constexpr int C_BYTES = 256 * CB;
+    static constexpr int S_BYTES = 1024 * S_DMA;
+    static constexpr int STAGE = A_BYTES + C_BYTES + S_BYTES;
+    static constexpr int D = A_BYTES / 1024 / 4 + C_DMA + S_DMA;  // DMAs per wave per stage
+};
+constexpr int ring_bytes(int wqt) { return NS * (wqt == WQ_F8 ? Fmt<WQ_F8>::STAGE : Fmt<WQ_Q4>::STAGE); }
+template <int WQ>
+__device__ __forceinline__ int cswz(int rho) { return WQ == WQ_F8 ? (rho >> 1) & 3 : (rho >> 2) & 1; }
+}  // namespace wq
+
+// one stage of one lane's codes for its two 32-column blocks, with their scales (and offsets)
+template <int WQ>
+struct BStage;
+template <>
+struct BStage<WQ_Q4> {
+    u32x4 q[2];
+    float s[2], b[2];
+    __device__ __forceinline__ u32x4 deq(int j, int st) const { return dequant8(q[j][st], s[j], b[j]); }
+};
+template <>
+struct BStage<WQ_F8> {
+    u32x4 q[2][2];  // block j: 32 codes; step st is words 2(st%2), 2(st%2)+1 of q[j][st/2]
+    float s[2];
+    __device__ __forceinline__ u32x4 deq(int j, int st) const {
+        return dequant_f8x8(q[j][st >> 1][2 * (st & 1)], q[j][st >> 1][2 * (st & 1) + 1], s[j]);
+    }
+};
+
+template <int WQ, bool SWIGLU>
+__global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     using namespace dma;
-    using q4t::NQ;
-    constexpr int BM = q4t::BM;
+    using F = wq::Fmt<WQ>;
+    constexpr int NS = wq::NS;
+    constexpr int BM = wq::BM;
     constexpr int MT = BM / 32;                // 32-row blocks per wave (all rows of the tile)
-    constexpr int A_BYTES = BM * ROWB;
-    constexpr int A_DMA = A_BYTES / 1024 / 4;  // DMA instructions per wave per stage
-    static_assert(q4t::ring_bytes() <= LDS_MAX, "ring exceeds LDS");
+    constexpr int A_BYTES = wq::A_BYTES;
+    constexpr int A_DMA = A_BYTES / 1024 / 4;  // activation DMAs per wave per stage
+    constexpr int D = F::D;
+    static_assert(NS * F::STAGE <= LDS_MAX, "ring exceeds LDS");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const GroupedArgs& a = ta.a;
@@ -363,6 +428,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5;
 
+    // activation DMA sources, as gemm_dma
     const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
     uint32_t a_off[A_DMA];
 #pragma unroll
@@ -379,44 +445,98 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
             a_off[j] = ((uint32_t)row * (uint32_t)a.ldh + c * 8) * 2u;
         }
     }
-    // output column of B block j for this lane: GEMM-1 gate (j = 0) and up (j = 1) rows of
-    // column 32 w + lane % 32; GEMM-2 rows 64 w + 32 j + lane % 32.  The expert's matrices are
-    // uniform bases; per lane only 32-bit offsets within them are kept.
-    const int64_t eq = (int64_t)g * N * (KD / 8), es = (int64_t)g * N * (KD / 64);
-    const uint32_t* qb0 = (const uint32_t*)(SWIGLU ? a.wg : a.wd) + eq;
-    const uint32_t* qb1 = (const uint32_t*)(SWIGLU ? a.wu : a.wd) + eq;
-    const bf16_t* sb0 = (SWIGLU ? a.sg : a.sd) + es;
-    const bf16_t* sb1 = (SWIGLU ? a.su : a.sd) + es;
-    const bf16_t* bb0 = (SWIGLU ? a.bg : a.bd) + es;
-    const bf16_t* bb1 = (SWIGLU ? a.bu : a.bd) + es;
-    int32_t ncol[2];
-    uint32_t qoff[2], soff[2];
+
+    // weight row (output column) of block j of this wave at in-block index i: GEMM-1 gate (j = 0)
+    // and up (j = 1) rows of column 32 w + i; GEMM-2 rows 64 w + 32 j + i.  Columns past N are
+    // computed from row N - 1 and never stored.
+    auto wcol = [&](int j, int i) -> int32_t { return n0 + (SWIGLU ? wave * 32 : wave * 64 + j * 32) + i; };
+    auto wrow = [&](int j, int i) -> int32_t { const int32_t n = wcol(j, i); return n < N ? n : N - 1; };
+    const void* wb[2] = {SWIGLU ? a.wg : a.wd, SWIGLU ? a.wu : a.wd};
+    // code DMA t of this wave: lane -> weight row rho = 64 w + t * ROWS_PER_DMA + lane / (CB/16),
+    // LDS chunk p = lane % (CB/16), holding logical chunk p ^ cswz(rho); per lane a 32-bit byte
+    // offset of (row, chunk) within the expert's code matrix
+    constexpr int CPR = F::CB / 16;  // chunks per weight row per stage
+    uint32_t c_off[F::C_DMA];
+    const char* c_base[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        ncol[j] = n0 + (SWIGLU ? wave * 32 : wave * 64 + j * 32) + (lane & 31);
-        const int32_t n = ncol[j] < N ? ncol[j] : N - 1;  // columns past N are computed, never stored
-        qoff[j] = (uint32_t)n * (uint32_t)(KD / 8) + half * 4;
-        soff[j] = (uint32_t)n * (uint32_t)(KD / 64);
+    for (int j = 0; j < 2; ++j) c_base[j] = (const char*)wb[j] + (int64_t)g * N * (WQ == WQ_F8 ? KD : KD / 2);
+#pragma unroll
+    for (int t = 0; t < F::C_DMA; ++t) {
+        const int rho = wave * 64 + t * F::ROWS_PER_DMA + lane / CPR;
+        const int jj = (rho >> 5) & 1, i = rho & 31;
+        const int cl = (lane % CPR) ^ wq::cswz<WQ>(rho);
+        const uint32_t row_bytes = WQ == WQ_F8 ? (uint32_t)KD : (uint32_t)KD / 2;
+        c_off[t] = (uint32_t)wrow(jj, i) * row_bytes + cl * 16;
     }
-    struct BStage {
-        u32x4 q[2];
-        bf16_t s[2], b[2];
-    };
-    auto load_b = [&](int kt, BStage& st) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            st.q[j] = *(const u32x4*)((j ? qb1 : qb0) + qoff[j] + kt * 8);
-            st.s[j] = (j ? sb1 : sb0)[soff[j] + kt];
-            st.b[j] = (j ? bb1 : bb0)[soff[j] + kt];
-        }
-    };
-    auto issue_a = [&](int kt) {
-        char* st = smem + (kt % NQ) * A_BYTES;
+    // side-data sources: lane -> weight row rho = 64 w + lane (block lane / 32, column lane % 32)
+    const int sj = lane >> 5, si = lane & 31;
+    const int32_t srow = wrow(sj, si);
+    const float* fs_ptr = nullptr;          // fp8: scale of (srow's block row, stage's k block)
+    const uint32_t* qs_ptr = nullptr;       // 4-bit: words holding the scale / offset
+    const uint32_t* qb_ptr = nullptr;
+    int32_t nq = 0;                         // 4-bit: element index of (srow, group 0)
+    if constexpr (WQ == WQ_F8) {
+        const int64_t nbo = (N + 127) / 128, nbi = (KD + 127) / 128;
+        const float* base = (SWIGLU ? (sj ? a.fsu : a.fsg) : a.fsd) + (int64_t)g * nbo * nbi;
+        fs_ptr = base + (int64_t)(srow / 128) * nbi;
+    } else {
+        // the element counts N * KD / 64 per expert are even (N is a multiple of 64), so the
+        // aligned word holding any element lies inside the array
+        const int64_t es = (int64_t)g * N * (KD / 64);
+        qs_ptr = (const uint32_t*)((SWIGLU ? (sj ? a.su : a.sg) : a.sd) + es);
+        qb_ptr = (const uint32_t*)((SWIGLU ? (sj ? a.bu : a.bg) : a.bd) + es);
+        nq = srow * (KD / 64);
+    }
+
+    auto issue = [&](int kt) {
+        char* st = smem + (kt % NS) * F::STAGE;
         const char* ab = (const char*)(a_base + kt * BKD);
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
             __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[j]),
                                              DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024), 16, 0, 0);
+        char* cst = st + A_BYTES + wave * 64 * F::CB;
+#pragma unroll
+        for (int t = 0; t < F::C_DMA; ++t) {
+            const int jj = ((t * F::ROWS_PER_DMA) >> 5) & 1;  // block of this instruction's rows
+            __builtin_amdgcn_global_load_lds((const void*)(c_base[jj] + c_off[t] + kt * F::CB),
+                                             DSMOE_LDS_PTR(cst + t * 1024), 16, 0, 0);
+        }
+        char* sst = st + A_BYTES + F::C_BYTES + wave * 256;
+        if constexpr (WQ == WQ_F8) {
+            __builtin_amdgcn_global_load_lds((const void*)(fs_ptr + (kt >> 1)), DSMOE_LDS_PTR(sst), 4, 0, 0);
+        } else {
+            const int32_t e = (nq + kt) >> 1;
+            __builtin_amdgcn_global_load_lds((const void*)(qs_ptr + e), DSMOE_LDS_PTR(sst), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(qb_ptr + e), DSMOE_LDS_PTR(sst + 1024), 4, 0, 0);
+        }
+    };
+
+    // this lane's codes and scales of stage kt, from LDS
+    using BS = BStage<WQ>;
+    auto read_b = [&](int kt, BS& bs) {
+        const char* st = smem + (kt % NS) * F::STAGE;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int rho = wave * 64 + j * 32 + (lane & 31);
+            const char* row = st + A_BYTES + rho * F::CB;
+            const int sw = wq::cswz<WQ>(rho);
+            const char* side = st + A_BYTES + F::C_BYTES + rho * 4;
+            if constexpr (WQ == WQ_F8) {
+                bs.q[j][0] = *(const u32x4*)(row + (((2 * half) ^ sw) << 4));
+                bs.q[j][1] = *(const u32x4*)(row + (((2 * half + 1) ^ sw) << 4));
+                bs.s[j] = *(const float*)side;
+            } else {
+                bs.q[j] = *(const u32x4*)(row + ((half ^ sw) << 4));
+                // the row's element for this stage is (its group index + kt); odd ones are the
+                // word's upper half
+                const int32_t nqj = wrow(j, lane & 31) * (KD / 64) + kt;
+                const uint32_t sw32 = *(const uint32_t*)side, bw32 = *(const uint32_t*)(side + 1024);
+                const int sh = (nqj & 1) * 16;
+                bs.s[j] = bf16_to_f32((bf16_t)(sw32 >> sh));
+                bs.b[j] = bf16_to_f32((bf16_t)(bw32 >> sh));
+            }
+        }
     };
 
     f32x16 acc[MT][2];
@@ -426,14 +546,13 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
     const int nk = KD / BKD;  // >= 1
     bf16x8 fa[2][MT], fb[2][2];
     // operands of step s of stage kt: activations from LDS, weights dequantised from registers
-    auto frags = [&](int kt, int s, int buf, const BStage& bs) {
-        const char* st = smem + (kt % NQ) * A_BYTES;
+    auto frags = [&](int kt, int s, int buf, const BS& bs) {
+        const char* st = smem + (kt % NS) * F::STAGE;
         const int c = 4 * half + s;
 #pragma unroll
         for (int i = 0; i < MT; ++i) fa[buf][i] = as_bf16x8(*(const u32x4*)(st + off(i * 32 + (lane & 31), c)));
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            fb[buf][j] = as_bf16x8(dequant8(bs.q[j][s], bf16_to_f32(bs.s[j]), bf16_to_f32(bs.b[j])));
+        for (int j = 0; j < 2; ++j) fb[buf][j] = as_bf16x8(bs.deq(j, s));
     };
     auto mfma_step = [&](int buf) {
 #pragma unroll
@@ -442,37 +561,33 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
     };
-    // one stage; `cur` holds its codes, `nxt` those of stage kt+1 (landed by the barrier)
-    auto stage = [&](int kt, BStage& cur, const BStage& nxt) {
-        frags(kt, 1, 1, cur);
+    // One stage.  At the barrier everything but the newest D operations (stage kt+2, issued
+    // during stage kt-1) has landed: stage kt+1 is complete in LDS, and every wave is done with
+    // stage kt's slot, which then receives stage kt+3.  Past the last stage the DMA repeats
+    // stage nk-1 into its own slot (the same bytes; never consumed), so every path issues the
+    // same sequence and the counts stay exact.
+    BS bs;
+    auto stage = [&](int kt) {
+        frags(kt, 1, 1, bs);
         mfma_step(0);
-        frags(kt, 2, 0, cur);
+        frags(kt, 2, 0, bs);
         mfma_step(1);
-        frags(kt, 3, 1, cur);
+        frags(kt, 3, 1, bs);
         mfma_step(0);
-        const bool next = kt + 1 < nk;
-        if (next) {
-            // A(kt+2) (issued last, during stage kt-1) may still fly; all older loads must land
-            if (kt >= 1 && kt + 2 < nk) wait_vm_barrier<A_DMA>();
-            else wait_vm_barrier<0>();
-            if (kt + 2 < nk) load_b(kt + 2, cur);  // cur's codes are all dequantised
-            if (kt + NQ < nk) issue_a(kt + NQ);    // the slot of stage kt is fully read
-            frags(kt + 1, 0, 0, nxt);
-        }
+        wait_vm_barrier<D>();
+        issue(kt + NS < nk ? kt + NS : nk - 1);
+        const int kn = kt + 1 < nk ? kt + 1 : nk - 1;
+        read_b(kn, bs);
+        frags(kn, 0, 0, bs);
         mfma_step(1);
     };
 
-    BStage b0, b1;
-    const int pro = min(nk, NQ);
-    for (int j = 0; j < pro; ++j) issue_a(j);
-    load_b(0, b0);
-    if (nk > 1) load_b(1, b1);
-    wait_vm_barrier<0>();
-    frags(0, 0, 0, b0);
-    for (int kt = 0; kt < nk; kt += 2) {  // two code sets, alternating by stage parity
-        stage(kt, b0, b1);
-        if (kt + 1 < nk) stage(kt + 1, b1, b0);
-    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) issue(j < nk ? j : nk - 1);
+    wait_vm_barrier<(NS - 1) * D>();
+    read_b(0, bs);
+    frags(0, 0, 0, bs);
+    for (int kt = 0; kt < nk; ++kt) stage(kt);
 
     // the accumulators of the last MFMAs are read right away: give the MFMA-to-VALU wait states
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
@@ -487,7 +602,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_q4(TileArgs ta) {
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
-            const int32_t col = ncol[j];
+            const int32_t col = wcol(j, lane & 31);
             if (col >= N) continue;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -552,11 +667,11 @@ hipError_t launch_dma_t(const TileArgs& ta, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool SW>
-hipError_t launch_dma_q4_t(const TileArgs& ta, hipStream_t s) {
-    const size_t lds = (size_t)q4t::ring_bytes();
+template <int WQ, bool SW>
+hipError_t launch_dma_wq_t(const TileArgs& ta, hipStream_t s) {
+    const size_t lds = (size_t)wq::ring_bytes(WQ);
     const unsigned grid = (unsigned)(((ta.nwg + 7) / 8) * 8);
-    hipLaunchKernelGGL((gemm_dma_q4<SW>), dim3(grid), dim3(THREADS), lds, s, ta);
+    hipLaunchKernelGGL((gemm_dma_wq<WQ, SW>), dim3(grid), dim3(THREADS), lds, s, ta);
     return hipGetLastError();
 }
 
@@ -570,18 +685,20 @@ int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM) {
 
 // largest dynamic LDS any tiled kernel of this tile height uses
 int32_t tiled_lds_bytes(int32_t BM) {
-    const int32_t dma_ring = dma::ring_bytes(BM), q4_ring = q4t::ring_bytes();
-    return BM == q4t::BM && q4_ring > dma_ring ? q4_ring : dma_ring;
+    const int32_t dma_ring = dma::ring_bytes(BM), wq_ring = wq::ring_bytes(WQ_F8);
+    return BM == wq::BM && wq_ring > dma_ring ? wq_ring : dma_ring;
 }
 
 hipError_t configure_tiled_kernels() {
     // allow the large dynamic LDS allocations (up to 128 KB) of the tiled kernels
     const void* ks[] = {
-        (const void*)gemm_dma<256, true>, (const void*)gemm_dma<256, false>, (const void*)gemm_dma<128, true>,
-        (const void*)gemm_dma<128, false>, (const void*)gemm_dma_q4<true>,   (const void*)gemm_dma_q4<false>,
+        (const void*)gemm_dma<256, true>,           (const void*)gemm_dma<256, false>,
+        (const void*)gemm_dma<128, true>,           (const void*)gemm_dma<128, false>,
+        (const void*)gemm_dma_wq<WQ_Q4, true>,      (const void*)gemm_dma_wq<WQ_Q4, false>,
+        (const void*)gemm_dma_wq<WQ_F8, true>,      (const void*)gemm_dma_wq<WQ_F8, false>,
     };
-    const int bms[] = {256, 256, 128, 128, 128, 128};
-    for (int i = 0; i < 6; ++i) {
+    const int bms[] = {256, 256, 128, 128, 128, 128, 128, 128};
+    for (int i = 0; i < 8; ++i) {
         hipError_t e = hipFuncSetAttribute(ks[i], hipFuncAttributeMaxDynamicSharedMemorySize, tiled_lds_bytes(bms[i]));
         if (e != hipSuccess) return e;
     }
@@ -608,14 +725,15 @@ hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32
     const int32_t out_cols = gemm1 ? NB / 2 : NB;
     ta.col_tiles = (N + out_cols - 1) / out_cols;
     ta.nwg = max_tiles * ta.col_tiles;
-    const bool q4 = wdt == MOE_Q4G64;
-    if (!q4) {
+    if (wdt == MOE_BF16) {
         if (BM == 256) return gemm1 ? launch_dma_t<256, true>(ta, s) : launch_dma_t<256, false>(ta, s);
         return gemm1 ? launch_dma_t<128, true>(ta, s) : launch_dma_t<128, false>(ta, s);
     }
-    // 4-bit layers always use tiles of 128 rows (plan_tiles)
+    // quantised layers always use tiles of 128 rows (plan_tiles)
     if (BM != 128) return hipErrorInvalidValue;
-    return gemm1 ? launch_dma_q4_t<true>(ta, s) : launch_dma_q4_t<false>(ta, s);
+    if (wdt == MOE_FP8) return gemm1 ? launch_dma_wq_t<WQ_F8, true>(ta, s) : launch_dma_wq_t<WQ_F8, false>(ta, s);
+    if (wdt == MOE_Q4G64) return gemm1 ? launch_dma_wq_t<WQ_Q4, true>(ta, s) : launch_dma_wq_t<WQ_Q4, false>(ta, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dsmoe

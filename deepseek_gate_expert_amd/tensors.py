@@ -1,7 +1,7 @@
 """Host -> device marshalling for the MoE layer binding.
 
 Converts numpy arrays in the storage conventions of the input generator (fp32, bf16 bit
-patterns as uint16, 4-bit codes as uint32) into torch device tensors, and bundles the device
+patterns as uint16, 4-bit codes as uint32, fp8 codes as uint8) into torch device tensors, and bundles the device
 weights of one layer with its descriptor and workspace.  No arithmetic of the layer lives here.
 """
 from __future__ import annotations
@@ -12,15 +12,15 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_OK, MOE_Q4G64, MOE_ROUTE_DEEPSEEK, MOE_ROUTE_SOFTMAX, LayerDesc, layer_desc,
+from . import (MOE_BF16, MOE_F32, MOE_FP8, MOE_OK, MOE_Q4G64, MOE_ROUTE_DEEPSEEK, MOE_ROUTE_SOFTMAX, LayerDesc, layer_desc,
                moe_forward, moe_forward_workspace_size, moe_strerror)
 
-_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "q4": MOE_Q4G64}
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "q4": MOE_Q4G64, "fp8": MOE_FP8}
 
 
 def to_device(a: np.ndarray, device, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """numpy -> device tensor: float32 -> float32, uint16 (bf16 bits) -> bfloat16,
-    uint32 -> int32 (same bits), int32 -> int32."""
+    uint32 -> int32 (same bits), int32 -> int32, uint8 (fp8 codes) -> uint8."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.float32:
         t = torch.from_numpy(a)
@@ -28,6 +28,8 @@ def to_device(a: np.ndarray, device, out: Optional[torch.Tensor] = None) -> torc
         t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
     elif a.dtype in (np.uint32, np.int32):
         t = torch.from_numpy(a.view(np.int32))
+    elif a.dtype == np.uint8:
+        t = torch.from_numpy(a)
     else:
         raise TypeError(f"unsupported host dtype {a.dtype}")
     if out is not None:

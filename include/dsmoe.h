@@ -50,6 +50,7 @@ extern "C" {
 #define MOE_F32 0   /* IEEE binary32 */
 #define MOE_BF16 1  /* bfloat16 (uint16 bit patterns) */
 #define MOE_Q4G64 2 /* 4-bit affine, groups of 64 along the input axis (expert weights only) */
+#define MOE_FP8 3   /* OCP E4M3 codes, one fp32 scale per 128 x 128 block (expert weights only) */
 
 /* gate kinds (moe_layer_desc.route_kind) */
 #define MOE_ROUTE_DEEPSEEK 0 /* sigmoid gate with correction bias and groups (moe_route_deepseek) */
@@ -76,7 +77,7 @@ typedef struct moe_layer_desc {
     int32_t I;           /* routed expert intermediate size */
     int32_t I_shared;    /* shared expert intermediate size; 0 = no shared expert */
     int32_t act_dtype;   /* MOE_F32 or MOE_BF16: x, y, router weight and shared weights */
-    int32_t expert_dtype;/* MOE_F32 (with act F32), MOE_BF16 or MOE_Q4G64 (with act BF16) */
+    int32_t expert_dtype;/* MOE_F32 (with act F32); MOE_BF16, MOE_Q4G64 or MOE_FP8 (with act BF16) */
     moe_route_params route; /* the softmax gate reads only route.top_k */
     int32_t route_kind;  /* MOE_ROUTE_DEEPSEEK or MOE_ROUTE_SOFTMAX */
 } moe_layer_desc;
@@ -85,6 +86,11 @@ typedef struct moe_layer_desc {
  *   w_gate, w_up: [E, I, H]; w_down: [E, H, I] in expert_dtype.
  *   MOE_Q4G64: w_* are uint32 [E, out, in/8] holding eight 4-bit codes q (element i of a row at
  *   bits 4*(i%8) of word i/8); s_* and b_* are bf16 [E, out, in/64]; the weight is s*q + b.
+ *   MOE_FP8: w_* are uint8 [E, out, in] OCP E4M3 codes (bias 7, no infinities; NaN codes are
+ *   outside the contract); s_* are fp32 [E, ceil(out/128), ceil(in/128)], one scale per
+ *   128 x 128 block; the weight is value(code) * scale -- the load-time dequantisation of fp8
+ *   checkpoints ([Epic56] weight loading), done here in registers: the kernels multiply in fp32
+ *   and round the product to bf16 (nearest even) before the bf16 matrix products.  b_* ignored.
  *   For the other dtypes s_* and b_* are ignored. */
 typedef struct moe_expert_weights {
     const void* w_gate;
@@ -190,14 +196,15 @@ int moe_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* 
  *                                                      that goes through silu)
  * Steps, all on `stream`: router logits (as moe_router_logits) -> gate (as moe_route_deepseek,
  * or moe_route_softmax when route_kind is MOE_ROUTE_SOFTMAX) -> dispatch (as moe_dispatch) ->
- * grouped gate/up GEMM with SwiGLU in the epilogue -> grouped down GEMM -> combine.  For bf16
- * and 4-bit layers with T > 64, each grouped GEMM is two kernels: weight streaming for the
+ * grouped gate/up GEMM with SwiGLU in the epilogue -> grouped down GEMM -> combine.  For bf16,
+ * 4-bit and fp8 layers with T > 64, each grouped GEMM is two kernels: weight streaming for the
  * expert groups of at most 64 rows, MFMA tiles for the larger groups and the shared expert.
  * The combine adds, per token and output element, the (gated) shared expert's output and then
  * the K weighted expert outputs in j order in fp32, with no atomics.
  * Precision: bf16 layers run bf16 MFMA with fp32 accumulation; the SwiGLU intermediate and the
  * per-expert outputs are rounded to bf16; y is rounded to act_dtype (nearest-even).  4-bit
- * weights are dequantised in registers (s*q + b, rounded to bf16) before the MFMA.
+ * weights are dequantised in registers (s*q + b, rounded to bf16) before the MFMA; fp8 weights
+ * likewise (value * block scale in fp32, rounded to bf16).
  *   d:            shapes, dtypes and gate parameters (host)
  *   x:            [T, H] act_dtype (device)          router_w: [E, H] act_dtype (device)
  *   bias:         fp32 [E] (device; may be NULL with the softmax gate)
@@ -210,9 +217,10 @@ int moe_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* 
  *   scores_out:   NULL or fp32 [T, top_k] (device, written): the gate's weights
  *   workspace:    device scratch, at least moe_forward_workspace_size(d) bytes, 256-byte aligned
  * Errors: -1 for invalid shapes/params/pointers (as above, plus H, I < 1, I_shared < 0, a
- * dtype combination other than F32/F32, BF16/BF16, BF16/Q4G64, and for MOE_Q4G64 missing
- * scales); -3 for a small workspace; -4 for E > MOE_MAX_EXPERTS, top_k > MOE_MAX_TOP_K,
- * T*top_k + T >= 2^31, or (bf16 / 4-bit layers) H, I or I_shared not a multiple of 64.
+ * dtype combination other than F32/F32, BF16/BF16, BF16/Q4G64, BF16/FP8, and for MOE_Q4G64
+ * missing scales or offsets, for MOE_FP8 missing scales); -3 for a small workspace; -4 for
+ * E > MOE_MAX_EXPERTS, top_k > MOE_MAX_TOP_K, T*top_k + T >= 2^31, or (bf16 / 4-bit / fp8
+ * layers) H, I or I_shared not a multiple of 64.
  * moe_forward_workspace_size returns 0 for a descriptor that moe_forward would reject.
  */
 size_t moe_forward_workspace_size(const moe_layer_desc* d);

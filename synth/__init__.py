@@ -4,7 +4,7 @@ This package only generates inputs; it holds none of the layer's arithmetic.
 Both the CPU oracle (``oracle/``) and the GPU path read what it produces, so
 the two sides see bit-identical inputs.  The generator itself is in
 ``synth.c`` (counter-based SplitMix64 + Box-Muller, see its header); this
-module wraps it and defines the five workloads.
+module wraps it and defines the workloads.
 
 Storage conventions (numpy):
   * fp32 tensors are ``float32`` arrays;
@@ -188,6 +188,11 @@ WORKLOADS = {
     # DeepSeek-V3 shapes with 4-bit routed experts
     "c4": Workload("c4", T=4096, H=7168, E=256, K=8, G=8, TG=4, I=2048, Is=2048, act="bf16", expert="q4",
                    bias_std=0.1, norm=True, rsf=2.5, seed=4, wseed=2),
+    # DeepSeek-V3 shapes with fp8 (E4M3, 128 x 128 block scales) routed experts: prefill and decode
+    "c5": Workload("c5", T=4096, H=7168, E=256, K=8, G=8, TG=4, I=2048, Is=2048, act="bf16", expert="fp8",
+                   bias_std=0.1, norm=True, rsf=2.5, seed=5, wseed=2),
+    "c6": Workload("c6", T=64, H=7168, E=256, K=8, G=8, TG=4, I=2048, Is=2048, act="bf16", expert="fp8",
+                   bias_std=0.1, norm=True, rsf=2.5, seed=6, wseed=2),
 }
 
 

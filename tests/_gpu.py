@@ -30,11 +30,13 @@ def act_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().double().cpu().numpy()
 
 
-TOL = {"f32": 1e-5, "bf16": 1e-2, "q4": 2e-2}
+# fp8 layers keep the bf16 bar: the kernels round each dequantised weight to bf16 (relative
+# error <= 2^-9, the oracle's weights are exact), which adds about 1e-3 to the relative L2 error
+TOL = {"f32": 1e-5, "bf16": 1e-2, "q4": 2e-2, "fp8": 1e-2}
 
 
 def tol_of(w) -> float:
-    return TOL["q4"] if w.expert == "q4" else TOL[w.act]
+    return TOL[w.expert] if w.expert in ("q4", "fp8") else TOL[w.act]
 
 
 _HOST, _DEVW = {}, {}

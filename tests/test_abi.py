@@ -151,6 +151,9 @@ FWD_REJECTS = {
     "null_w_gate": (dict(), dict(ew_null="w_gate")),
     "null_w_down": (dict(), dict(ew_null="w_down")),
     "q4_null_scale": (dict(expert_dtype=2), dict(q4=True, ew_null="s_up")),
+    "fp8_null_scale": (dict(expert_dtype=3), dict(q4=True, ew_null="s_down")),
+    "f32_act_with_fp8_experts": (dict(act_dtype=0, expert_dtype=3), {}),
+    "unknown_expert_dtype": (dict(expert_dtype=4), {}),
     "shared_weights_missing": (dict(), dict(shared=False)),
     "shared_weights_without_shared_expert": (dict(I_shared=0), dict(shared=True)),
     "null_workspace": (dict(), dict(ws=None)),
@@ -163,6 +166,18 @@ def test_forward_reject_matrix(lib, name):
     kw, fkw = FWD_REJECTS[name]
     d = desc(**kw)
     assert forward(lib, d, **fkw) == dg.MOE_ERR_INVALID
+
+
+def test_forward_fp8_ignores_offsets(lib):
+    """fp8 layers read only the block scales: NULL offsets pass the argument checks (the short
+    workspace is then the first error, still found on the host)."""
+    d = desc(expert_dtype=3)
+    need = lib.moe_forward_workspace_size(ctypes.byref(d))
+    assert need > 0
+    ew = dg.ExpertWeights(P, P, P, P, None, P, None, P, None)
+    sw = dg.SharedWeights(P, P, P)
+    assert lib.moe_forward(ctypes.byref(d), P, P, P, None, ctypes.byref(ew), ctypes.byref(sw), P, None, None, P,
+                           need - 1, None) == dg.MOE_ERR_WORKSPACE
 
 
 def test_forward_workspace_too_small(lib):

@@ -3,7 +3,7 @@
 Pages: "Epic: Engine Inference Core Stage E - MoE + hybrid families" (gather_mm / gather_qmm
 expert dispatch, shared experts always active) and the gate page's merge recommendation
 (router -> route -> switch_glu -> combine).  Bar: routing indices bit-exact, gate weights
-within relative 1e-6, y within relative L2 1e-5 (fp32 layers), 1e-2 (bf16) and 2e-2 (4-bit),
+within relative 1e-6, y within relative L2 1e-5 (fp32 layers), 1e-2 (bf16, fp8) and 2e-2 (4-bit),
 against the oracle's fp64 expert math.  The five workloads run at full size; for the two
 largest the oracle computes y on a sample of tokens (its routing covers every token).
 """
@@ -40,7 +40,7 @@ def test_layer_full(name):
     assert err <= tol_of(w)
 
 
-@pytest.mark.parametrize("name,n_sample", [("c3", 24), ("c4", 24)])
+@pytest.mark.parametrize("name,n_sample", [("c3", 24), ("c4", 24), ("c5", 24), ("c6", 16)])
 def test_layer_full_size_sampled(name, n_sample):
     w = synth.WORKLOADS[name]
     log(f"[layer] {w.desc} (sampled)")
@@ -111,6 +111,15 @@ EDGE = [
     ("softmax_gated_q4", C1.with_(T=300, H=256, I=128, Is=128, expert="q4", route="softmax", shared_gate=True,
                                   planted=0)),
     ("softmax_gated_f32", synth.WORKLOADS["c0"].with_(route="softmax", shared_gate=True)),
+    # fp8 experts: streamed, ragged blocks (H = 320: k blocks of 128, 128, 64 and a 64-wide tail
+    # step; I = 192: output blocks of 128 and 64), tiled, tiled with long groups, softmax + gate
+    ("fp8_small", C1.with_(T=50, expert="fp8", planted=0)),
+    ("fp8_tail", C1.with_(T=20, H=320, I=192, Is=192, expert="fp8", planted=0)),
+    ("tiled_fp8", C1.with_(T=400, H=512, I=256, Is=192, expert="fp8", planted=0)),
+    ("tiled_fp8_ragged_blocks", C1.with_(T=500, H=320, I=192, Is=128, expert="fp8", planted=0)),
+    ("tiled_rows_fp8", C1.with_(T=2048, H=256, I=128, Is=128, expert="fp8", planted=0)),
+    ("softmax_gated_fp8", C1.with_(T=300, H=256, I=128, Is=128, expert="fp8", route="softmax", shared_gate=True,
+                                   planted=0)),
 ]
 
 
