@@ -445,15 +445,13 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     }
     a.stream_max_rows = tp.on ? STREAM_MAX_ROWS : 0x7fffffff;
     const int32_t rdt = quant ? d->expert_dtype : MOE_BF16;
-    const int32_t split = quant ? E : gend;  // quantised routed groups vs the bf16 (shared) group
-    // weight-streaming kernels of one expert-GEMM pass (groups of at most stream_max_rows rows)
+    const int32_t split = quant ? E : gend;  // tiled: quantised routed groups vs the bf16 (shared) group
+    // weight-streaming kernels of one expert-GEMM pass (groups of at most stream_max_rows rows);
+    // one launch covers the routed groups and the shared expert, which streams its bf16 weights
+    // also in quantised layers
     auto streamed = [&](bool first) -> int {
         if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));
-        int r = hip_rc(first ? launch_gemm1_bf16(a, 0, split, rdt, s) : launch_gemm2_bf16(a, 0, split, rdt, s));
-        if (!r && split < gend)
-            r = hip_rc(first ? launch_gemm1_bf16(a, split, gend, MOE_BF16, s)
-                             : launch_gemm2_bf16(a, split, gend, MOE_BF16, s));
-        return r;
+        return hip_rc(first ? launch_gemm1_bf16(a, 0, gend, rdt, s) : launch_gemm2_bf16(a, 0, gend, rdt, s));
     };
     // tiled kernels of one pass (the other groups)
     auto tiled = [&](bool first) -> int {

@@ -87,8 +87,8 @@ hipError_t launch_route(const float* logits, int64_t T, int32_t E, const float* 
 int32_t dispatch_blocks(int64_t TK);
 hipError_t launch_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_slot, int32_t* slot_row, int32_t* blk, hipStream_t s);
-// bf16-activation expert GEMMs for groups [g0, g1); wdt = weight dtype of those groups
-// (MOE_BF16, MOE_Q4G64 or MOE_FP8; the shared group E is always bf16)
+// bf16-activation expert GEMMs for groups [g0, g1); wdt = weight dtype of the routed groups
+// (MOE_BF16, MOE_Q4G64 or MOE_FP8; the shared group E is always bf16 and may be in the range)
 hipError_t launch_gemm1_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s);
 hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s);
 // fp32 layers: all routed rows and the shared rows in one launch each

@@ -206,12 +206,11 @@ template <int N>
 __device__ __forceinline__ void s_wait_barrier() { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory"); }
 
 // GEMM-1 (G1): h = SwiGLU of x rows against W_gate / W_up;  GEMM-2: o = h rows against W_down.
-// grid: x = ceil(N / 64) column blocks (N = I or Is, resp. H), y = groups [g0, g0 + gridDim.y).
-// N is a multiple of 64 (bf16 and 4-bit layers), so every wave of a live workgroup has columns.
+// One workgroup's share of group g: 64 output columns (blockIdx.x), every row of the group.
+// N is a multiple of 64 (bf16, 4-bit and fp8 layers), so every wave of a live workgroup has
+// columns.  As: the activation ring (three buffers, two steps ahead).
 template <int WF, bool G1>
-__global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
-    __shared__ __attribute__((aligned(1024))) char As[3 * S_TILE];  // activation ring, two steps ahead
-    const int32_t g = g0 + blockIdx.y;
+__device__ __forceinline__ void stream_body(const GroupedArgs& a, int32_t g, char* As) {
     int32_t r0, cnt;
     group_rows(a, g, r0, cnt);
     if (cnt <= 0 || cnt > a.stream_max_rows) return;
@@ -366,6 +365,20 @@ __global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
             }
         }
     }
+}
+
+// grid: x = ceil(N / 64) column blocks (N = max(I, Is), resp. H), y = groups [g0, g0 + gridDim.y).
+// The shared expert (group E) always has bf16 weights: in a launch over quantised routed groups
+// it takes the bf16 body, so it streams beside the routed groups instead of in a launch of its
+// own with only N / 64 workgroups.
+template <int WF, bool G1>
+__global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
+    __shared__ __attribute__((aligned(1024))) char As[3 * S_TILE];
+    const int32_t g = g0 + blockIdx.y;
+    if (WF != WF_BF16 && g == a.E)  // workgroup-uniform
+        stream_body<WF_BF16, G1>(a, g, As);
+    else
+        stream_body<WF, G1>(a, g, As);
 }
 
 }  // namespace

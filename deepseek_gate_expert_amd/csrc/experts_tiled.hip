@@ -114,6 +114,8 @@ constexpr int BKD = 64;        // k per stage: a whole 128-byte line of every ro
 constexpr int ROWB = 128;      // bytes per LDS row
 constexpr int NST = 2;         // ring depth
 constexpr int LDS_MAX = 160 * 1024;
+constexpr int THREADS = 512;   // 8 waves, two per SIMD
+constexpr int PRODUCERS = 4;   // waves 0..3 issue the DMA, one per SIMD
 constexpr int ring_bytes(int bm) { return NST * (bm + 256) * ROWB; }
 // chunk swizzle: the 8 chunks of row r are permuted by (r ^ r/8) mod 8, which keeps the MFMA
 // operand reads free of bank conflicts whether a ds_read_b128 phase serves 8 lanes (rows r..r+7)
@@ -140,34 +142,30 @@ __device__ __forceinline__ void wait_stages(int later) {
 }
 
 // Epilogue of a 32x32-MFMA tile: rows [mrow, mrow + 32 MT) of the group, the wave's output
-// columns.  GEMM-1 holds gate accumulators in j = 0, 1 and up in j = 2, 3 (64 output columns
-// per wave) and writes bf16(silu(gate) * up) to h; GEMM-2 writes its 128 columns to o.
+// columns.  GEMM-1 holds the gate accumulators in j = 0 and up in j = 1 (32 output columns per
+// wave) and writes bf16(silu(gate) * up) to h; GEMM-2 writes its 64 columns to o.
 template <int MT, bool SWIGLU>
-__device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16 (&acc)[MT][4], int32_t r0,
+__device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16 (&acc)[MT][2], int32_t r0,
                                               int32_t cnt, int32_t mrow, int32_t n0, int32_t N, int wn, int lane) {
     const int col_l = lane & 31, rgrp = (lane >> 5) * 4;
     if (SWIGLU) {
         bf16_t* h = (bf16_t*)a.h;
+        const int32_t col = n0 + wn * 32 + col_l;
+        if (col >= N) return;
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int32_t col = n0 + wn * 64 + j * 32 + col_l;
-                if (col >= N) continue;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int32_t rr = mrow + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                    if (rr < cnt)
-                        h[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[i][j][v]) * acc[i][j + 2][v]);
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int32_t rr = mrow + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
+                if (rr < cnt) h[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
             }
     } else {
         bf16_t* o = (bf16_t*)a.o;
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int32_t col = n0 + wn * 128 + j * 32 + col_l;
+            for (int j = 0; j < 2; ++j) {
+                const int32_t col = n0 + wn * 64 + j * 32 + col_l;
                 if (col >= N) continue;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
@@ -179,13 +177,13 @@ __device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16
 }
 
 template <int BM, bool SWIGLU>
-__global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
+__global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
     using namespace dma;
     constexpr int WM = BM / 2;
     constexpr int MT = WM / 32;
     constexpr int A_BYTES = BM * ROWB, B_BYTES = NB * ROWB, ST_BYTES = A_BYTES + B_BYTES;
-    constexpr int A_DMA = A_BYTES / 1024 / 4;  // DMA instructions per wave per stage
-    constexpr int B_DMA = B_BYTES / 1024 / 4;
+    constexpr int A_DMA = A_BYTES / 1024 / PRODUCERS;  // DMA instructions per producer wave per stage
+    constexpr int B_DMA = B_BYTES / 1024 / PRODUCERS;
     constexpr int D = A_DMA + B_DMA;
     static_assert(ring_bytes(BM) <= LDS_MAX, "ring exceeds LDS");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -212,15 +210,16 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
 
     // the wave index is uniform: keep it scalar so the DMA destinations (M0) are scalar too
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int pw = wave & (PRODUCERS - 1);  // producer index (waves >= PRODUCERS issue no DMA)
 
-    // ---- DMA sources: instruction j of this wave fills LDS rows [8 (wave*X + j), +8); lane i
+    // ---- DMA sources: instruction j of producer pw fills LDS rows [8 (pw*X + j), +8); lane i
     // writes chunk i % 8 of row i / 8, so it fetches the logical chunk that the swizzle puts there
     const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
     uint32_t a_off[A_DMA];
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
-        const int r = (wave * A_DMA + j) * 8 + (lane >> 3);
+        const int r = (pw * A_DMA + j) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz(r);
         int32_t rr = m0 + r;
         rr = rr < cnt ? rr : cnt - 1;  // rows past the group are computed, never stored
@@ -245,7 +244,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
     uint32_t b_off[B_DMA];
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
-        const int br = (wave * B_DMA + j) * 8 + (lane >> 3);
+        const int br = (pw * B_DMA + j) * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz(br);
         int32_t n = n0 + (SWIGLU ? br % (NB / 2) : br);
         n = n < N ? n : N - 1;  // columns past N are computed, never stored
@@ -255,30 +254,31 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
     // DMA sources are a uniform base (advanced by the stage) plus a per-lane 32-bit byte offset,
     // so no per-lane 64-bit address arithmetic is issued per instruction
     auto issue = [&](int kt) {
+        if (wave >= PRODUCERS) return;  // wave-uniform
         char* st = smem + (kt % NST) * ST_BYTES;
         const int32_t k0 = kt * BKD;
         const char* ab = (const char*)(a_base + k0);
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
             __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[j]),
-                                             DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024), 16, 0, 0);
+                                             DSMOE_LDS_PTR(st + (pw * A_DMA + j) * 1024), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < B_DMA; ++j) {
-            const int br0 = (wave * B_DMA + j) * 8;
+            const int br0 = (pw * B_DMA + j) * 8;
             const char* wb = (const char*)(((SWIGLU && br0 >= NB / 2) ? wb1 : wb0) + k0);
             __builtin_amdgcn_global_load_lds((const void*)(wb + b_off[j]),
-                                             DSMOE_LDS_PTR(st + A_BYTES + (wave * B_DMA + j) * 1024), 16, 0, 0);
+                                             DSMOE_LDS_PTR(st + A_BYTES + (pw * B_DMA + j) * 1024), 16, 0, 0);
         }
     };
 
-    f32x16 acc[MT][4];
+    f32x16 acc[MT][2];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = f32x16{};
+    // B rows of the wave's two 32-row blocks: GEMM-1 gate rows (j = 0) and up rows (j = 1) of
+    // output columns [32 wn, 32 wn + 32); GEMM-2 rows [64 wn, 64 wn + 64)
+    int brow[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    int brow[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) brow[j] = SWIGLU ? (j < 2 ? 0 : NB / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+    for (int j = 0; j < 2; ++j) brow[j] = SWIGLU ? j * (NB / 2) + wn * 32 : wn * 64 + j * 32;
 
     // Software pipeline over k16 steps (four per stage): the fragments of the next step are read
     // from LDS while the current step's MFMAs run.  The wait + barrier that publishes stage kt+1
@@ -286,12 +286,12 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
     // stage kt are all in registers, so its slot is refilled with stage kt+NST right away and
     // those loads have the next four steps to land.
     const int nk = KD / BKD;  // >= 1
-    bf16x8 fa[2][MT], fb[2][4];
+    bf16x8 fa[2][MT], fb[2][2];
     auto read_frags = [&](int kt, int s, int buf) {
         const char* st = smem + (kt % NST) * ST_BYTES;
         const int c = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
             fb[buf][j] = as_bf16x8(*(const u32x4*)(st + A_BYTES + off(brow[j] + (lane & 31), c)));
 #pragma unroll
         for (int i = 0; i < MT; ++i) fa[buf][i] = as_bf16x8(*(const u32x4*)(st + off(wm * WM + i * 32 + (lane & 31), c)));
@@ -303,14 +303,14 @@ __global__ __launch_bounds__(THREADS) void gemm_dma(TileArgs ta) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (then_read) {
             read_frags(rkt, rs, rbuf);
-            __builtin_amdgcn_sched_group_barrier(0x100, MT + 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, MT + 2, 0);
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
                 if (i | j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, MT * 4 - 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MT * 2 - 1, 0);
     };
     const int pro = min(nk, NST);  // stages issued up front
     for (int j = 0; j < pro; ++j) issue(j);
@@ -663,7 +663,7 @@ template <int BM, bool SW>
 hipError_t launch_dma_t(const TileArgs& ta, hipStream_t s) {
     const size_t lds = (size_t)dma::ring_bytes(BM);
     const unsigned grid = (unsigned)(((ta.nwg + 7) / 8) * 8);
-    hipLaunchKernelGGL((gemm_dma<BM, SW>), dim3(grid), dim3(THREADS), lds, s, ta);
+    hipLaunchKernelGGL((gemm_dma<BM, SW>), dim3(grid), dim3(dma::THREADS), lds, s, ta);
     return hipGetLastError();
 }
 
