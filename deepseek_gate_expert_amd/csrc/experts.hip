@@ -41,14 +41,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float b) {
     u32x4 r;
     // codes 2j and 2j+1 are the low and high nibble of byte j: split the nibbles into bytes once,
-    // then convert each byte directly (v_cvt_f32_ubyte{0..3})
+    // then convert each byte directly
     const uint32_t lo4 = w & 0x0F0F0F0Fu, hi4 = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float lo = __builtin_fmaf(s, (float)((lo4 >> (8 * j)) & 0xFFu), b);
-        const float hi = __builtin_fmaf(s, (float)((hi4 >> (8 * j)) & 0xFFu), b);
-        r[j] = pack_bf16x2(lo, hi);
-    }
+    r[0] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<0>(lo4), b), __builtin_fmaf(s, cvt_ubyte<0>(hi4), b));
+    r[1] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<1>(lo4), b), __builtin_fmaf(s, cvt_ubyte<1>(hi4), b));
+    r[2] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<2>(lo4), b), __builtin_fmaf(s, cvt_ubyte<2>(hi4), b));
+    r[3] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<3>(lo4), b), __builtin_fmaf(s, cvt_ubyte<3>(hi4), b));
     return as_bf16x8(r);
 }
 

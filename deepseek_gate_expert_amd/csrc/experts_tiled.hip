@@ -33,14 +33,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float b) {
     u32x4 r;
     // codes 2j and 2j+1 are the low and high nibble of byte j: split the nibbles into bytes once,
-    // then convert each byte directly (v_cvt_f32_ubyte{0..3})
+    // then convert each byte directly
     const uint32_t lo4 = w & 0x0F0F0F0Fu, hi4 = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float lo = __builtin_fmaf(s, (float)((lo4 >> (8 * j)) & 0xFFu), b);
-        const float hi = __builtin_fmaf(s, (float)((hi4 >> (8 * j)) & 0xFFu), b);
-        r[j] = pack_bf16x2(lo, hi);
-    }
+    r[0] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<0>(lo4), b), __builtin_fmaf(s, cvt_ubyte<0>(hi4), b));
+    r[1] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<1>(lo4), b), __builtin_fmaf(s, cvt_ubyte<1>(hi4), b));
+    r[2] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<2>(lo4), b), __builtin_fmaf(s, cvt_ubyte<2>(hi4), b));
+    r[3] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<3>(lo4), b), __builtin_fmaf(s, cvt_ubyte<3>(hi4), b));
     return r;
 }
 
@@ -337,8 +335,8 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 // Quantised weights, tiles of 128 rows: 4-bit (affine, groups of 64 along the reduction axis)
 // or fp8 (OCP E4M3 codes, one fp32 scale per 128 x 128 block).  Same tile shape and tile list
 // as gemm_dma.  Every operand of a 64-k stage -- the activation rows, the weight codes and the
-// scales (and 4-bit offsets) -- enters LDS by DMA, in a ring of three stages (stages kt+1 and
-// kt+2 in flight while kt is computed).  With no register loads in the loop the compiler inserts
+// scales (and 4-bit offsets) -- enters LDS by DMA, in a ring of stages (three for 4-bit, two
+// for fp8: stages up to kt+NS-1 in flight while kt is computed).  With no register loads in the loop the compiler inserts
 // no waits of its own: the only waits are the explicit count + barrier per stage.  (Loading the
 // codes into registers beside an LDS DMA ring made the compiler wait for every outstanding load
 // before each use of them, which exposed the full memory latency once per stage.)
@@ -364,10 +362,12 @@ enum { WQ_Q4 = 0, WQ_F8 = 1 };
 
 namespace wq {
 constexpr int BM = 128;
-constexpr int NS = 3;                          // ring depth
 constexpr int A_BYTES = BM * dma::ROWB;        // activations of one stage
 template <int WQ>
 struct Fmt {
+    // ring depth: three stages for 4-bit (two workgroups of 78 KB still share a CU), two for
+    // fp8 (so that two workgroups of 66 KB fit; three stages would hold one per CU)
+    static constexpr int NS = WQ == WQ_F8 ? 2 : 3;
     static constexpr int CB = WQ == WQ_F8 ? 64 : 32;            // code bytes per weight row per stage
     static constexpr int ROWS_PER_DMA = 1024 / CB;              // weight rows per DMA instruction
     static constexpr int C_DMA = 64 / ROWS_PER_DMA;             // code DMAs per wave per stage
@@ -377,7 +377,9 @@ struct Fmt {
     static constexpr int STAGE = A_BYTES + C_BYTES + S_BYTES;
     static constexpr int D = A_BYTES / 1024 / 4 + C_DMA + S_DMA;  // DMAs per wave per stage
 };
-constexpr int ring_bytes(int wqt) { return NS * (wqt == WQ_F8 ? Fmt<WQ_F8>::STAGE : Fmt<WQ_Q4>::STAGE); }
+constexpr int ring_bytes(int wqt) {
+    return wqt == WQ_F8 ? Fmt<WQ_F8>::NS * Fmt<WQ_F8>::STAGE : Fmt<WQ_Q4>::NS * Fmt<WQ_Q4>::STAGE;
+}
 template <int WQ>
 __device__ __forceinline__ int cswz(int rho) { return WQ == WQ_F8 ? (rho >> 1) & 3 : (rho >> 2) & 1; }
 }  // namespace wq
@@ -404,13 +406,13 @@ template <int WQ, bool SWIGLU>
 __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     using namespace dma;
     using F = wq::Fmt<WQ>;
-    constexpr int NS = wq::NS;
+    constexpr int NS = F::NS;
     constexpr int BM = wq::BM;
     constexpr int MT = BM / 32;                // 32-row blocks per wave (all rows of the tile)
     constexpr int A_BYTES = wq::A_BYTES;
     constexpr int A_DMA = A_BYTES / 1024 / 4;  // activation DMAs per wave per stage
     constexpr int D = F::D;
-    static_assert(NS * F::STAGE <= LDS_MAX, "ring exceeds LDS");
+    static_assert(NS >= 2 && NS * F::STAGE <= LDS_MAX, "ring depth / size");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const GroupedArgs& a = ta.a;
@@ -561,9 +563,9 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
     };
-    // One stage.  At the barrier everything but the newest D operations (stage kt+2, issued
-    // during stage kt-1) has landed: stage kt+1 is complete in LDS, and every wave is done with
-    // stage kt's slot, which then receives stage kt+3.  Past the last stage the DMA repeats
+    // One stage.  At the barrier everything but the newest (NS-2) D operations (stage kt+NS-1,
+    // issued during stage kt-1) has landed: stage kt+1 is complete in LDS, and every wave is done
+    // with stage kt's slot, which then receives stage kt+NS.  Past the last stage the DMA repeats
     // stage nk-1 into its own slot (the same bytes; never consumed), so every path issues the
     // same sequence and the counts stay exact.
     BS bs;
@@ -574,7 +576,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
         mfma_step(1);
         frags(kt, 3, 1, bs);
         mfma_step(0);
-        wait_vm_barrier<D>();
+        wait_vm_barrier<(NS - 2) * D>();
         issue(kt + NS < nk ? kt + NS : nk - 1);
         const int kn = kt + 1 < nk ? kt + 1 : nk - 1;
         read_b(kn, bs);
@@ -685,7 +687,7 @@ int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM) {
 
 // largest dynamic LDS any tiled kernel of this tile height uses
 int32_t tiled_lds_bytes(int32_t BM) {
-    const int32_t dma_ring = dma::ring_bytes(BM), wq_ring = wq::ring_bytes(WQ_F8);
+    const int32_t dma_ring = dma::ring_bytes(BM), wq_ring = max(wq::ring_bytes(WQ_F8), wq::ring_bytes(WQ_Q4));
     return BM == wq::BM && wq_ring > dma_ring ? wq_ring : dma_ring;
 }
 
