@@ -294,40 +294,47 @@ __device__ __forceinline__ void stream_body(const GroupedArgs& a, int32_t g, cha
             }
         };
 
-        // One full step: publish its activations, start the loads of step s+2, run its MFMAs.
-        // Activations (three LDS buffers) and weights (three rotating register sets) both run
-        // two steps ahead; per wave the issue order is A(s+2), W(s+2) during step s, so at the
-        // top of step s everything but A(s+1) and W(s+1) (the newest DMA + WL operations; the
-        // DMA only for the waves that copy rows) must have landed.  Past the end the loads
+        // One full step: publish its activations, start the loads of steps s+2 (activations) and
+        // s+D (weights), run its MFMAs.  Activations run two steps ahead in three LDS buffers;
+        // weights run D steps ahead in D+1 rotating register sets (D = 3 for fp8, whose steps
+        // carry half the bytes of bf16 ones, so more of them must be in flight; else 2).  Per wave
+        // the issue order is A(s+2), W(s+D) during step s.  At the top of step s, A(s) and W(s)
+        // must have landed; what may stay in flight is everything issued after them -- for
+        // D = 2: A(s+1), W(s+1); for D > 2 (W(s) is older than A(s)): W(s+D-2), A(s+1),
+        // W(s+D-1) -- the DMA counted only for the waves that copy rows.  Past the end the loads
         // repeat the last step (L2 hits, never consumed) instead of being skipped: with the same
         // load sequence on every path the compiler's own waits for the weight registers stay
         // exact rather than falling back to waiting for everything.
         constexpr int WL = NW * (WF == WF_BF16 ? 4 : 3);  // vector-memory operations of one load_full
-        auto step = [&](int s, const W (&cur)[NW], W (&nxt2)[NW]) {
-            if (wave < nrb) s_wait_barrier<4 + WL>();  // wave-uniform; both arms hold one barrier
-            else s_wait_barrier<WL>();
+        constexpr int D = WF == WF_F8 ? 3 : 2;
+        constexpr int NWS = D + 1;
+        constexpr int LATER_COPY = D == 2 ? 4 + WL : 4 + 2 * WL;  // waves that copy activation rows
+        constexpr int LATER_NOCOPY = (D - 1) * WL;                // waves that do not
+        auto step = [&](int s, const W (&cur)[NW], W (&nxt)[NW]) {
+            if (wave < nrb) s_wait_barrier<LATER_COPY>();  // wave-uniform; both arms hold one barrier
+            else s_wait_barrier<LATER_NOCOPY>();
             // the buffer written here was last read in step s-1; past the last step it is not
             // read again in this chunk
             issue_a(min(s + 2, nsteps - 1), (s + 2) % 3);
-            load_full(min(s + 2, nfull - 1), nxt2);
+            load_full(min(s + D, nfull - 1), nxt);
             compute(std::integral_constant<int, 4>{}, s % 3, cur);
         };
 
         __syncthreads();  // the previous chunk's reads of every buffer are done
-        W wa[NW], wb[NW], wc[NW];
+        W ws[NWS][NW];
         issue_a(0, 0);
         if (nfull > 0) {
-            // both prologue steps are issued unconditionally (with one full step the second
-            // repeats step 0 and is never used, unless it is the tail's activations), so the
-            // compiler's own wait before the loop's first MFMAs sees the same load order on
-            // entry as around the loop and stays exact
-            load_full(0, wa);
+            // the prologue loads are issued unconditionally (past the last full step they repeat
+            // it and are never used), so the compiler's own wait before the loop's first MFMAs
+            // sees the same load order on entry as around the loop and stays exact
+            load_full(0, ws[0]);
             issue_a(min(1, nsteps - 1), 1);
-            load_full(nfull > 1 ? 1 : 0, wb);
-            for (int s = 0; s < nfull; s += 3) {  // rotate through three register sets
-                step(s, wa, wc);
-                if (s + 1 < nfull) step(s + 1, wb, wa);
-                if (s + 2 < nfull) step(s + 2, wc, wb);
+#pragma unroll
+            for (int j = 1; j < D; ++j) load_full(min(j, nfull - 1), ws[j]);
+            for (int s = 0; s < nfull; s += NWS) {  // W(k) lives in set k % NWS
+#pragma unroll
+                for (int u = 0; u < NWS; ++u)
+                    if (s + u < nfull) step(s + u, ws[u], ws[(u + D) % NWS]);
             }
         }
         if (tail) {  // a 64-wide last step (reduction lengths of 64 mod 128 only): weights unprefetched
