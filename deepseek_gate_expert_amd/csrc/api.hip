@@ -43,15 +43,16 @@ constexpr int32_t STREAM_MAX_ROWS = 64;
 
 struct TilePlan {
     bool on;
-    int32_t BM;
-    int32_t max_tiles;
+    int32_t BM;         // tile height of the routed groups
+    int32_t BMs;        // tile height of the shared expert
+    int32_t max_tiles;  // bound on the tile list (for the smaller of the two heights)
 };
 
 // Shapes-only decision (no device reads): tiles of 256 rows when the average group is large
 // (bf16 weights only: the 4-bit and fp8 kernel keeps its dequantised operands in registers and
 // runs 128-row tiles).
 TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
-    TilePlan p{false, 128, 0};
+    TilePlan p{false, 128, 128, 0};
     if (d->act_dtype != MOE_BF16 || d->T <= STREAM_MAX_ROWS) return p;
     // the tiled kernels address activation and weight rows with 32-bit byte offsets
     const int64_t rows = d->T * d->route.top_k + d->T;
@@ -63,7 +64,10 @@ TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     p.on = true;
     const int64_t avg = d->T * d->route.top_k / d->E;
     p.BM = (allow256 && avg >= 192 && d->expert_dtype == MOE_BF16) ? 256 : 128;
-    p.max_tiles = tiled_max_tiles(d->T, d->route.top_k, d->E, p.BM);
+    // bf16 layers run the shared expert in the routed groups' launch; quantised layers give its
+    // bf16 weights a launch of their own, with 256-row tiles once it has that many rows
+    p.BMs = d->expert_dtype == MOE_BF16 ? p.BM : (allow256 && d->T >= 256 ? 256 : 128);
+    p.max_tiles = tiled_max_tiles(d->T, d->route.top_k, d->E, p.BM < p.BMs ? p.BM : p.BMs);
     return p;
 }
 
@@ -251,7 +255,7 @@ int moe_dense_mlp(int64_t T, int32_t H, int32_t I, int32_t act_dtype, const void
     const int32_t max_tiles = tiled_max_tiles(T, 0, 0, BM);
     int32_t* tile_count = (int32_t*)(ws + L.tiles);
     int32_t* tile_info = tile_count + 64;
-    if ((rc = hip_rc(launch_tiles(a, BM, STREAM_MAX_ROWS, tile_count, tile_info, s)))) return rc;
+    if ((rc = hip_rc(launch_tiles(a, BM, BM, STREAM_MAX_ROWS, tile_count, tile_info, s)))) return rc;
     if ((rc = hip_rc(launch_gemm_tiled(a, true, BM, 0, 1, MOE_BF16, tile_count, tile_info, max_tiles, s))))
         return rc;
     return hip_rc(launch_gemm_tiled(a, false, BM, 0, 1, MOE_BF16, tile_count, tile_info, max_tiles, s));
@@ -438,7 +442,7 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     const int32_t gend = E + (d->I_shared > 0 ? 1 : 0);
     const bool f32 = d->act_dtype == MOE_F32;
     const bool quant = d->expert_dtype == MOE_Q4G64 || d->expert_dtype == MOE_FP8;
-    TilePlan tp{false, 128, 0};
+    TilePlan tp{false, 128, 128, 0};
     if (!f32) {
         const int ts = tiled_state();
         if (ts != 3) tp = plan_tiles(d, ts == 1);
@@ -458,11 +462,11 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
         if (!tp.on) return MOE_OK;
         int r = hip_rc(launch_gemm_tiled(a, first, tp.BM, 0, split, rdt, tile_count, tile_info, tp.max_tiles, s));
         if (!r && split < gend)
-            r = hip_rc(launch_gemm_tiled(a, first, tp.BM, split, gend, MOE_BF16, tile_count, tile_info,
+            r = hip_rc(launch_gemm_tiled(a, first, tp.BMs, split, gend, MOE_BF16, tile_count, tile_info,
                                          tp.max_tiles, s));
         return r;
     };
-    if (tp.on && (rc = hip_rc(launch_tiles(a, tp.BM, STREAM_MAX_ROWS, tile_count, tile_info, s)))) return rc;
+    if (tp.on && (rc = hip_rc(launch_tiles(a, tp.BM, tp.BMs, STREAM_MAX_ROWS, tile_count, tile_info, s)))) return rc;
     // With tiles on, the GEMM1 / GEMM2 stage events bracket the tiled kernels only (the
     // dominant kernels of prefill layers); the streaming kernels run right before them.
     for (int pass = 0; pass < 2; ++pass) {

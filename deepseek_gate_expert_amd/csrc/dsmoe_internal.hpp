@@ -109,8 +109,9 @@ hipError_t launch_gemm2_f32(const GroupedArgs& a, hipStream_t s);
 int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM);
 int32_t tiled_lds_bytes(int32_t BM);
 hipError_t configure_tiled_kernels();
-hipError_t launch_tiles(const GroupedArgs& a, int32_t BM, int32_t min_rows, int32_t* tile_count, int32_t* tile_info,
-                        hipStream_t s);
+// tile list: routed groups in tiles of BM rows, the shared expert (group E) in tiles of BMs rows
+hipError_t launch_tiles(const GroupedArgs& a, int32_t BM, int32_t BMs, int32_t min_rows, int32_t* tile_count,
+                        int32_t* tile_info, hipStream_t s);
 hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32_t g0, int32_t g1, int32_t wdt,
                              const int32_t* tile_count, const int32_t* tile_info, int32_t max_tiles, hipStream_t s);
 hipError_t launch_route_softmax(const float* logits, int64_t T, int32_t E, int32_t K, int32_t* inds, float* scores,

@@ -620,18 +620,20 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
 }
 
 // Tile list: every group in [0, E] (E = shared expert) with more than `min_rows` rows gets
-// ceil(rows / BM) tiles, in group order.  One workgroup; group 1024 (only possible with
-// E == 1024 plus a shared expert) is appended by thread 0.
+// ceil(rows / BM) tiles (ceil(T / BMs) for the shared expert, whose tiles a launch of their own
+// may compute with a different tile height), in group order.  One workgroup; group 1024 (only
+// possible with E == 1024 plus a shared expert) is appended by thread 0.
 __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ offsets, int32_t E, int64_t T,
-                                                     int32_t has_shared, int32_t BM, int32_t min_rows,
+                                                     int32_t has_shared, int32_t BM, int32_t BMs, int32_t min_rows,
                                                      int32_t* __restrict__ tile_count,
                                                      int32_t* __restrict__ tile_info) {
     __shared__ int32_t buf[1024];
     const int t = threadIdx.x;
     const int32_t ng = E + has_shared;
+    auto bm_of = [&](int32_t g) -> int32_t { return g < E ? BM : BMs; };
     auto ntiles = [&](int32_t g) -> int32_t {
         const int32_t cnt = g < E ? offsets[g + 1] - offsets[g] : (int32_t)T;
-        return cnt > min_rows ? (cnt + BM - 1) / BM : 0;
+        return cnt > min_rows ? (cnt + bm_of(g) - 1) / bm_of(g) : 0;
     };
     const int32_t n = t < ng ? ntiles(t) : 0;
     buf[t] = n;
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
     const int32_t start = buf[t] - n;
     for (int32_t m = 0; m < n; ++m) {
         tile_info[2 * (start + m)] = t;
-        tile_info[2 * (start + m) + 1] = m * BM;
+        tile_info[2 * (start + m) + 1] = m * bm_of(t);
     }
     if (t == 0) {
         int32_t total = buf[1023];
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
             const int32_t nn = ntiles(1024);
             for (int32_t m = 0; m < nn; ++m) {
                 tile_info[2 * (total + m)] = 1024;
-                tile_info[2 * (total + m) + 1] = m * BM;
+                tile_info[2 * (total + m) + 1] = m * bm_of(1024);
             }
             total += nn;
         }
@@ -707,10 +709,10 @@ hipError_t configure_tiled_kernels() {
     return hipSuccess;
 }
 
-hipError_t launch_tiles(const GroupedArgs& a, int32_t BM, int32_t min_rows, int32_t* tile_count, int32_t* tile_info,
-                        hipStream_t s) {
-    hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is > 0 ? 1 : 0, BM, min_rows,
-                       tile_count, tile_info);
+hipError_t launch_tiles(const GroupedArgs& a, int32_t BM, int32_t BMs, int32_t min_rows, int32_t* tile_count,
+                        int32_t* tile_info, hipStream_t s) {
+    hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is > 0 ? 1 : 0, BM, BMs,
+                       min_rows, tile_count, tile_info);
     return hipGetLastError();
 }
 
