@@ -41,13 +41,22 @@ __global__ __launch_bounds__(CB) void combine_bf16(const bf16_t* __restrict__ o,
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
         }
-        for (int32_t j = 0; j < K; ++j) {
-            const u32x4 v = *(const u32x4*)(o + (int64_t)row[j] * H + c);
-            const float wj = w[j];
+        // the K expert rows in batches of eight: a batch's loads are issued together, then added
+        // in j order
+        for (int32_t j0 = 0; j0 < K; j0 += 8) {
+            u32x4 v[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = __builtin_fmaf(wj, bf16_to_f32((bf16_t)(v[i] & 0xffffu)), acc[2 * i]);
-                acc[2 * i + 1] = __builtin_fmaf(wj, bf16_to_f32((bf16_t)(v[i] >> 16)), acc[2 * i + 1]);
+            for (int u = 0; u < 8; ++u)
+                v[u] = j0 + u < K ? *(const u32x4*)(o + (int64_t)row[j0 + u] * H + c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u >= K) break;
+                const float wj = w[j0 + u];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] = __builtin_fmaf(wj, bf16_to_f32((bf16_t)(v[u][i] & 0xffffu)), acc[2 * i]);
+                    acc[2 * i + 1] = __builtin_fmaf(wj, bf16_to_f32((bf16_t)(v[u][i] >> 16)), acc[2 * i + 1]);
+                }
             }
         }
         u32x4 out;

@@ -39,12 +39,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk, i
                                                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
     __shared__ int32_t buf[1024];
     const int e = threadIdx.x;  // E <= 1024
+    constexpr int U = 16;       // column entries read before any is written back: the loads of a
+                                // batch are in flight together instead of one after each store
     int32_t tot = 0;
     if (e < E) {
-        for (int32_t b = 0; b < nblk; ++b) {
-            const int32_t c = blk[(int64_t)b * E + e];
-            blk[(int64_t)b * E + e] = tot;
-            tot += c;
+        for (int32_t b0 = 0; b0 < nblk; b0 += U) {
+            int32_t c[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) c[j] = b0 + j < nblk ? blk[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                if (b0 + j < nblk) blk[(int64_t)(b0 + j) * E + e] = tot;
+                tot += c[j];
+            }
         }
         counts[e] = tot;
     }
@@ -59,7 +66,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk, i
     const int32_t excl = buf[e] - tot;
     if (e < E) {
         offsets[e] = excl;
-        for (int32_t b = 0; b < nblk; ++b) blk[(int64_t)b * E + e] += excl;
+        for (int32_t b0 = 0; b0 < nblk; b0 += U) {
+            int32_t c[U];
+#pragma unroll
+            for (int j = 0; j < U; ++j) c[j] = b0 + j < nblk ? blk[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+                if (b0 + j < nblk) blk[(int64_t)(b0 + j) * E + e] = c[j] + excl;
+        }
     }
     if (e == 0) offsets[E] = TK;
 }
