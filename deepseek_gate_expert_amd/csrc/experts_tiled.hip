@@ -139,38 +139,51 @@ __device__ __forceinline__ void wait_stages(int later) {
     else wait_vm_barrier<D>();
 }
 
-// Epilogue of a 32x32-MFMA tile: rows [mrow, mrow + 32 MT) of the group, the wave's output
-// columns.  GEMM-1 holds the gate accumulators in j = 0 and up in j = 1 (32 output columns per
-// wave) and writes bf16(silu(gate) * up) to h; GEMM-2 writes its 64 columns to o.
-template <int MT, bool SWIGLU>
-__device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16 (&acc)[MT][2], int32_t r0,
-                                              int32_t cnt, int32_t mrow, int32_t n0, int32_t N, int wn, int lane) {
-    const int col_l = lane & 31, rgrp = (lane >> 5) * 4;
-    if (SWIGLU) {
-        bf16_t* h = (bf16_t*)a.h;
-        const int32_t col = n0 + wn * 32 + col_l;
-        if (col >= N) return;
+// Epilogue of a gemm_dma tile, staged through LDS (the stage ring is free once every wave has
+// left the k loop): each wave writes its bf16 results -- GEMM-1: bf16(silu(gate) * up), gate
+// accumulators in j = 0 and up in j = 1, 32 output columns per wave; GEMM-2: 64 columns -- into
+// a row-major image of the output tile, then all threads copy it out in 16-byte row pieces.
+// Written straight from the MFMA layout, every lane would store one column: 2-byte stores, 128
+// per lane for GEMM-2, which cost more than a tenth of the tile's time at K = 2048.  In the image
+// the 16-byte chunk c of row r sits at chunk c ^ (4 (r / 4 mod 2)), so the two rows one
+// ds_write_b16 touches (r and r + 4) fall in different banks.  Rows past the group and columns
+// past N are not stored.
+template <int BM, bool SWIGLU>
+__device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16 (&acc)[BM / 64][2], char* smem,
+                                              int32_t r0, int32_t cnt, int32_t m0, int32_t n0, int32_t N, int wm,
+                                              int wn, int tid) {
+    constexpr int MT = BM / 64;
+    constexpr int WM = BM / 2;
+    constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
+    constexpr int RB = OUT_COLS * 2;  // bytes per image row
+    constexpr int CPR = OUT_COLS / 8;  // 16-byte chunks per row
+    static_assert(BM * RB <= dma::ring_bytes(BM), "output image exceeds the ring");
+    const int lane = tid & 63, col_l = lane & 31, rsub = 4 * (lane >> 5);
+    auto cswz = [](int r) { return ((r >> 2) & 1) << 2; };
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave is done with the ring
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
+            const int col = SWIGLU ? wn * 32 + col_l : wn * 64 + j * 32 + col_l;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int32_t rr = mrow + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                if (rr < cnt) h[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
+                const int row = wm * WM + i * 32 + 8 * (v >> 2) + rsub + (v & 3);
+                const float val = SWIGLU ? silu_f(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
+                *(bf16_t*)(smem + row * RB + ((((col >> 3) ^ cswz(row)) << 4) | ((col & 7) << 1))) = f32_to_bf16(val);
             }
-    } else {
-        bf16_t* o = (bf16_t*)a.o;
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    bf16_t* dst = SWIGLU ? (bf16_t*)a.h : (bf16_t*)a.o;
+    const int64_t ld = SWIGLU ? a.ldh : a.H;
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int32_t col = n0 + wn * 64 + j * 32 + col_l;
-                if (col >= N) continue;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int32_t rr = mrow + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                    if (rr < cnt) o[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[i][j][v]);
-                }
-            }
+    for (int k = 0; k < BM * CPR / dma::THREADS; ++k) {
+        const int q = tid + k * dma::THREADS;
+        const int row = q / CPR, c = q % CPR;
+        const int32_t col = n0 + c * 8;
+        if (m0 + row >= cnt || col >= N) continue;
+        const u32x4 v = *(const u32x4*)(smem + row * RB + ((c ^ cswz(row)) << 4));
+        *(u32x4*)(dst + (int64_t)(r0 + m0 + row) * ld + col) = v;
     }
 }
 
@@ -327,7 +340,7 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
         mfma_step(1, next, kt + 1, 0, 0);
     }
 
-    tile_epilogue<MT, SWIGLU>(a, acc, r0, cnt, m0 + wm * WM, n0, N, wn, lane);
+    tile_epilogue<BM, SWIGLU>(a, acc, smem, r0, cnt, m0, n0, N, wm, wn, tid);
 }
 
 
