@@ -101,8 +101,8 @@ FwdLayout fwd_layout(const moe_layer_desc* d) {
     off += up(TK * 4);
     L.slot_row = off;
     off += up(TK * 4);
-    L.tiles = off;  // tile count + (group, row) pairs; sized for the smaller tile height
-    off += up(256 + 8 * (size_t)tiled_max_tiles(d->T, d->route.top_k, d->E, 128));
+    L.tiles = off;  // tile count + 16-byte tile entries; sized for the smaller tile height
+    off += up(256 + 16 * (size_t)tiled_max_tiles(d->T, d->route.top_k, d->E, 128));
     L.h = off;
     off += up(rows * ldh * el);
     L.o = off;
@@ -167,7 +167,7 @@ DenseLayout dense_layout(int64_t T, int32_t I, int32_t act) {
     const size_t el = act == MOE_F32 ? 4 : 2;
     size_t off = 0;
     L.tiles = off;
-    off += up(256 + 8 * (size_t)tiled_max_tiles(T, 0, 0, 128));
+    off += up(256 + 16 * (size_t)tiled_max_tiles(T, 0, 0, 128));
     L.h = off;
     off += up((size_t)T * (size_t)I * el);
     L.total = off;
@@ -384,7 +384,7 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     int32_t* sorted_slot = (int32_t*)(ws + L.sorted_slot);
     int32_t* slot_row = (int32_t*)(ws + L.slot_row);
     int32_t* tile_count = (int32_t*)(ws + L.tiles);
-    int32_t* tile_info = tile_count + 64;  // keep the pairs 256-byte aligned
+    int32_t* tile_info = tile_count + 64;  // keep the entries 256-byte aligned
 
     if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 0, s)))) return rc;
     if ((rc = hip_rc(launch_router(x, router_w, d->act_dtype, d->T, d->H, d->E, logit_offset, logits, s))))

@@ -36,6 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native 16-byte vector (promotes to VGPRs)
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 static_assert(sizeof(bf16x8) == 16, "bf16x8 is 16 bytes");
 

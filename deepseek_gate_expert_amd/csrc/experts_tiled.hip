@@ -63,7 +63,8 @@ __device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_r
 struct TileArgs {
     GroupedArgs a;
     const int32_t* tile_count;  // [1]
-    const int32_t* tile_info;   // [max_tiles][2]: group, first row within the group
+    const int32_t* tile_info;   // [max_tiles][4]: group, first row within the group, the group's
+                                //   first row in the row space, its row count
     int32_t g0, g1;             // groups handled by this launch
     int32_t col_tiles;          // output column tiles per row tile
     int32_t nwg;                // workgroups launched
@@ -202,17 +203,10 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
     const GroupedArgs& a = ta.a;
     int32_t tile, ct;
     if (!map_tile(ta, tile, ct)) return;
-    const int32_t g = ta.tile_info[2 * tile], m0 = ta.tile_info[2 * tile + 1];
+    const i32x4 ti = *(const i32x4*)(ta.tile_info + 4 * tile);  // group, first row, group rows
+    const int32_t g = ti[0], m0 = ti[1], r0 = ti[2], cnt = ti[3];
     if (g < ta.g0 || g >= ta.g1) return;
     const bool shared = g == a.E;
-    int32_t r0, cnt;
-    if (!shared) {
-        r0 = a.offsets[g];
-        cnt = a.offsets[g + 1] - r0;
-    } else {
-        r0 = a.TK;
-        cnt = (int32_t)a.T;
-    }
     const int32_t N = SWIGLU ? (shared ? a.Is : a.I) : a.H;
     const int32_t KD = SWIGLU ? a.H : (shared ? a.Is : a.I);
     constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
@@ -431,10 +425,9 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     const GroupedArgs& a = ta.a;
     int32_t tile, ct;
     if (!map_tile(ta, tile, ct)) return;
-    const int32_t g = ta.tile_info[2 * tile], m0 = ta.tile_info[2 * tile + 1];
+    const i32x4 ti = *(const i32x4*)(ta.tile_info + 4 * tile);  // group, first row, group rows
+    const int32_t g = ti[0], m0 = ti[1], r0 = ti[2], cnt = ti[3];
     if (g < ta.g0 || g >= ta.g1 || g >= a.E) return;  // routed groups only (the shared expert is bf16)
-    const int32_t r0 = a.offsets[g];
-    const int32_t cnt = a.offsets[g + 1] - r0;
     const int32_t N = SWIGLU ? a.I : a.H;
     const int32_t KD = SWIGLU ? a.H : a.I;
     constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
@@ -632,12 +625,14 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
         }
 }
 
-// Tile list: every group in [0, E] (E = shared expert) with more than `min_rows` rows gets
+// Tile list (offsets is read only for routed groups: it may be NULL when E == 0): every group in
+// [0, E] (E = shared expert) with more than `min_rows` rows gets
 // ceil(rows / BM) tiles (ceil(T / BMs) for the shared expert, whose tiles a launch of their own
 // may compute with a different tile height), in group order.  One workgroup; group 1024 (only
 // possible with E == 1024 plus a shared expert) is appended by thread 0.
 __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ offsets, int32_t E, int64_t T,
-                                                     int32_t has_shared, int32_t BM, int32_t BMs, int32_t min_rows,
+                                                     int32_t TK, int32_t has_shared, int32_t BM, int32_t BMs,
+                                                     int32_t min_rows,
                                                      int32_t* __restrict__ tile_count,
                                                      int32_t* __restrict__ tile_info) {
     __shared__ int32_t buf[1024];
@@ -658,18 +653,17 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
         __syncthreads();
     }
     const int32_t start = buf[t] - n;
-    for (int32_t m = 0; m < n; ++m) {
-        tile_info[2 * (start + m)] = t;
-        tile_info[2 * (start + m) + 1] = m * bm_of(t);
-    }
+    auto put = [&](int32_t i, int32_t g, int32_t m) {
+        const int32_t r0 = g < E ? offsets[g] : TK;  // the shared rows follow the routed ones
+        const int32_t cnt = g < E ? offsets[g + 1] - offsets[g] : (int32_t)T;
+        *(i32x4*)(tile_info + 4 * i) = i32x4{g, m * bm_of(g), r0, cnt};
+    };
+    for (int32_t m = 0; m < n; ++m) put(start + m, t, m);
     if (t == 0) {
         int32_t total = buf[1023];
         if (ng > 1024) {
             const int32_t nn = ntiles(1024);
-            for (int32_t m = 0; m < nn; ++m) {
-                tile_info[2 * (total + m)] = 1024;
-                tile_info[2 * (total + m) + 1] = m * bm_of(1024);
-            }
+            for (int32_t m = 0; m < nn; ++m) put(total + m, 1024, m);
             total += nn;
         }
         tile_count[0] = total;
@@ -724,8 +718,8 @@ hipError_t configure_tiled_kernels() {
 
 hipError_t launch_tiles(const GroupedArgs& a, int32_t BM, int32_t BMs, int32_t min_rows, int32_t* tile_count,
                         int32_t* tile_info, hipStream_t s) {
-    hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.Is > 0 ? 1 : 0, BM, BMs,
-                       min_rows, tile_count, tile_info);
+    hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.T, a.TK, a.Is > 0 ? 1 : 0, BM,
+                       BMs, min_rows, tile_count, tile_info);
     return hipGetLastError();
 }
 
