@@ -86,6 +86,8 @@ EDGE = [
     ("top_k_1", C1.with_(T=64, K=1, planted=0)),
     ("no_dropped_group", C1.with_(T=64, TG=4, planted=0)),
     ("K_above_kept", C1.with_(T=32, K=40, G=8, TG=2, planted=0)),
+    ("top_k_max_streamed", C1.with_(T=24, K=64, G=2, TG=1, planted=0)),  # top_k at its limit (64)
+    ("top_k_max_tiled", C1.with_(T=200, H=256, I=128, Is=128, K=64, G=2, TG=1, planted=0)),
     ("no_shared", C1.with_(T=48, Is=0, planted=0)),
     ("shared_narrower", C1.with_(T=48, I=256, Is=128, planted=0)),
     ("shared_wider", C1.with_(T=48, I=128, Is=320, planted=0)),
