@@ -49,7 +49,7 @@ struct TilePlan {
 };
 
 // Shapes-only decision (no device reads): tiles of 256 rows when the average group is large
-// (bf16 weights only: the 4-bit and fp8 kernel keeps its dequantised operands in registers and
+// (bf16 weights only: the 4-bit and fp8 kernel dequantises its operands in registers and
 // runs 128-row tiles).
 TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     TilePlan p{false, 128, 128, 0};

@@ -196,3 +196,23 @@ def test_layer_bias_changes_selection_not_weights():
     assert np.all(gi[:, 0] == 9)
     logits = oracle.router(x, r, "bf16")
     assert np.array_equal(gs[:, 0], oracle.sigmoid(logits[:, 9]))
+
+
+@pytest.mark.parametrize("T", [40, 300], ids=["streamed", "tiled"])
+def test_layer_fp8_every_code(T):
+    """fp8 weights whose codes cycle through all 254 finite E4M3 codes (both signs, subnormals,
+    the largest magnitude), so the in-register decode meets every code on both GEMM paths."""
+    w = C1.with_(T=T, H=256, I=128, Is=64, expert="fp8", planted=0)
+    w_, r, b, x, ex, sh, off = small_case(w)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    ex = dict(ex)
+    for k, nm in enumerate(("gate", "up", "down")):
+        n = ex[nm].size
+        ex[nm] = finite[(np.arange(n) * 7 + 31 * k) % len(finite)].reshape(ex[nm].shape)
+    log(f"[fp8 codes] T={T}")
+    y, gi, gs = run_small(w_, r, b, x, ex, sh, off)
+    y_ref, oi, os_, _ = oracle.forward_workload(w_, x, r, b, ex, sh, offset=off)
+    check_route(gi, gs, oi, os_)
+    err = rel_l2(act_to_f64(y), y_ref)
+    log(f"[fp8 codes] T={T} rel L2 {err:.3e}")
+    assert err <= tol_of(w_)
