@@ -33,8 +33,8 @@ METRIC = "MoE-layer tokens/sec (DeepSeek-V3 shape, bf16) + % HBM/MFMA peak"
 # 256 MiB device copy that main() runs first (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  The summaries
 # are kept with the kernel traces; an entry goes back to None whenever its kernel changes.
 TRAFFIC_GB = {
-    "c3": 8.57,  # gemm_dma<256, true>: 4,037,111 KiB fetched, 292,420 KiB written per launch
-    "c2": 7.47,  # stream_gemm<bf16, gate/up>: 3,644,559 KiB fetched, 2,305 KiB written per launch
+    "c3": 8.45,  # gemm_dma<256, true>: 3,978,947 KiB fetched, 292,420 KiB written per launch
+    "c2": 7.47,  # stream_gemm<bf16, gate/up>: 3,645,204 KiB fetched, 2,305 KiB written per launch
 }
 
 
