@@ -197,8 +197,10 @@ int moe_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* 
  * Steps, all on `stream`: router logits (as moe_router_logits) -> gate (as moe_route_deepseek,
  * or moe_route_softmax when route_kind is MOE_ROUTE_SOFTMAX) -> dispatch (as moe_dispatch) ->
  * grouped gate/up GEMM with SwiGLU in the epilogue -> grouped down GEMM -> combine.  For bf16,
- * 4-bit and fp8 layers with T > 64, each grouped GEMM is two kernels: weight streaming for the
- * expert groups of at most 64 rows, MFMA tiles for the larger groups and the shared expert.
+ * 4-bit and fp8 layers with T > 64, each grouped GEMM is split by group size: weight streaming for
+ * the expert groups of at most 64 rows, MFMA tiles for the larger groups and the shared expert
+ * (one tiled launch for bf16 layers; in 4-bit and fp8 layers the quantised routed groups and the
+ * bf16 shared expert have a tiled launch each).
  * The combine adds, per token and output element, the (gated) shared expert's output and then
  * the K weighted expert outputs in j order in fp32, with no atomics.
  * Precision: bf16 layers run bf16 MFMA with fp32 accumulation; the SwiGLU intermediate and the
@@ -255,7 +257,7 @@ int moe_dense_mlp(int64_t T, int32_t H, int32_t I, int32_t act_dtype, const void
  * the first kernel of `stage` and events[2*i + 1] right after the stage's last kernel, with
  * i = (moe_forward calls since the hook was set) mod n_pairs.  When a grouped GEMM is split
  * into streaming and tiled kernels (see moe_forward), the GEMM1 and GEMM2 pairs bracket the
- * tiled kernels only.  events are hipEvent_t handles
+ * tiled launches only.  events are hipEvent_t handles
  * owned by the caller (created with timing enabled) and must outlive the hook.  stage = -1 (or
  * n_pairs = 0) clears the hook.  The hook is process-wide and not thread-safe: set it only
  * while one thread drives moe_forward.  Errors: -1 for a stage out of range, n_pairs < 0, or
