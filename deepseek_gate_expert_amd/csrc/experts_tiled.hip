@@ -562,12 +562,21 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) fb[buf][j] = as_bf16x8(bs.deq(j, s));
     };
+    // the MFMAs of step `buf`, with the next step's operand work (issued just before, in program
+    // order) spread between them: its LDS reads first, then a few dequantisation instructions
+    // after each MFMA, so the vector ALU runs while the matrix core does
     auto mfma_step = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);  // LDS reads of the next step's A fragments
+#pragma unroll
+        for (int q = 0; q < 2 * MT; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, WQ == WQ_F8 ? 5 : 7, 0);  // then vector ALU work
+        }
     };
     // One stage.  At the barrier everything but the newest (NS-2) D operations (stage kt+NS-1,
     // issued during stage kt-1) has landed: stage kt+1 is complete in LDS, and every wave is done
