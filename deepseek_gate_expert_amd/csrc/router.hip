@@ -22,8 +22,6 @@ __device__ __forceinline__ float ld_act<float>(const float* p, int64_t i) { retu
 template <>
 __device__ __forceinline__ float ld_act<bf16_t>(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 
-constexpr int KC = 32;
-
 // 8 consecutive activations as fp32 (16- or 32-byte vector loads)
 template <typename TA>
 __device__ __forceinline__ void ld8(const TA* p, float (&v)[8]);
@@ -58,15 +56,18 @@ __device__ __forceinline__ void ld8_row(const TA* row, int32_t i, int32_t H, boo
 }
 
 // Many tokens: 256 threads, MT x NT register tile per thread (BM = 16 MT tokens x BN = 16 NT
-// experts per workgroup), k chunks of 32 staged in LDS as fp32 (k-major), double buffered: the
-// next chunk's global loads are in flight while the current chunk is multiplied.
-template <typename TA, int MT, int NT>
+// experts per workgroup), k chunks of KC staged in LDS as fp32 (k-major), double buffered: the
+// next chunk's global loads are in flight while the current chunk is multiplied.  Full chunks
+// run a fully unrolled k loop, so the LDS reads of later k steps issue ahead of the FMAs.
+template <typename TA, int MT, int NT, int KC>
 __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, const TA* __restrict__ w,
                                                      const float* __restrict__ off, float* __restrict__ logits,
                                                      int64_t T, int32_t H, int32_t E) {
     constexpr int BM = 16 * MT, BN = 16 * NT;
-    constexpr int XL = BM * KC / 8 / 256, WL = BN * KC / 8 / 256;  // 8-element loads per thread
-    static_assert(XL >= 1 && WL >= 1, "tile too small for the staging layout");
+    constexpr int LPR = KC / 8;                                     // 8-element loads per row
+    constexpr int XL = BM * LPR / 256, WL = BN * LPR / 256;  // 8-element loads per thread
+    static_assert(XL >= 1 && WL >= 1 && BM * LPR % 256 == 0 && BN * LPR % 256 == 0,
+                  "tile does not fit the staging layout");
     __shared__ float xs[2][KC][BM + 4];
     __shared__ float ws[2][KC][BN + 4];
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
@@ -74,20 +75,20 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
     const int32_t n0 = blockIdx.y * BN;
     const bool vec = (H % 8) == 0;
 
-    // staging assignment: load i of this thread covers row (tid + 256 i) / 4, k (tid % 4) * 8
+    // staging assignment: load i of this thread covers row (tid + 256 i) / LPR, k (tid % LPR) * 8
     const TA* xrow[XL];
     const TA* wrow[WL];
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
-        int64_t t = m0 + (tid + 256 * i) / 4;
+        int64_t t = m0 + (tid + 256 * i) / LPR;
         xrow[i] = x + (t < T ? t : T - 1) * H;
     }
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
-        int32_t e = n0 + (tid + 256 * i) / 4;
+        int32_t e = n0 + (tid + 256 * i) / LPR;
         wrow[i] = w + (int64_t)(e < E ? e : E - 1) * H;
     }
-    const int kq = (tid & 3) * 8;
+    const int kq = (tid % LPR) * 8;
     float xv[XL][8], wv[WL][8];
 
     float acc[MT][NT];
@@ -106,11 +107,11 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
 #pragma unroll
         for (int i = 0; i < XL; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xs[b][kq + j][(tid + 256 * i) / 4] = xv[i][j];
+            for (int j = 0; j < 8; ++j) xs[b][kq + j][(tid + 256 * i) / LPR] = xv[i][j];
 #pragma unroll
         for (int i = 0; i < WL; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ws[b][kq + j][(tid + 256 * i) / 4] = wv[i][j];
+            for (int j = 0; j < 8; ++j) ws[b][kq + j][(tid + 256 * i) / LPR] = wv[i][j];
         __syncthreads();
         if (c + 1 < nch) {
             const int32_t kn = (c + 1) * KC + kq;
@@ -119,8 +120,7 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
 #pragma unroll
             for (int i = 0; i < WL; ++i) ld8_row(wrow[i], kn, H, vec, wv[i]);
         }
-        const int kc = min(KC, H - c * KC);  // the zero tail of the last chunk is never used
-        for (int k = 0; k < kc; ++k) {
+        auto step = [&](int k) {
             float a[MT], bb[NT];
 #pragma unroll
             for (int i = 0; i < MT; ++i) a[i] = xs[b][k][ty * MT + i];
@@ -130,6 +130,13 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
             for (int i = 0; i < MT; ++i)
 #pragma unroll
                 for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
+        };
+        const int kc = min(KC, H - c * KC);  // the zero tail of the last chunk is never used
+        if (kc == KC) {
+#pragma unroll
+            for (int k = 0; k < KC; ++k) step(k);
+        } else {
+            for (int k = 0; k < kc; ++k) step(k);
         }
         // buffer b is rewritten two chunks later, after the next iteration's barrier
     }
@@ -227,12 +234,25 @@ hipError_t launch_gemv(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E
     return hipGetLastError();
 }
 
-template <typename TA, int MT, int NT>
+template <typename TA, int MT, int NT, int KC>
 hipError_t launch_t(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, const float* off, float* logits,
                     hipStream_t s) {
     const dim3 grid((unsigned)((T + 16 * MT - 1) / (16 * MT)), (E + 16 * NT - 1) / (16 * NT));
-    hipLaunchKernelGGL((router_kernel<TA, MT, NT>), grid, dim3(256), 0, s, x, w, off, logits, T, H, E);
+    hipLaunchKernelGGL((router_kernel<TA, MT, NT, KC>), grid, dim3(256), 0, s, x, w, off, logits, T, H, E);
     return hipGetLastError();
+}
+
+// Few tokens or few experts: one output per lane (GEMV shape).  Otherwise the largest register
+// tile that still gives at least 256 workgroups (one per CU): 4 x 4 (64 x 64 logits per
+// workgroup), then 2 x 4, then 2 x 2 with 64-k chunks.  The summation order is the same in all.
+template <typename TA>
+hipError_t route_shape(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, const float* off,
+                       float* logits, hipStream_t s) {
+    if (T <= 512 || E < 16) return launch_gemv<TA>(x, w, T, H, E, off, logits, s);
+    const int64_t ecols = (E + 63) / 64;
+    if (((T + 63) / 64) * ecols >= 256) return launch_t<TA, 4, 4, 32>(x, w, T, H, E, off, logits, s);
+    if (((T + 31) / 32) * ecols >= 256) return launch_t<TA, 2, 4, 64>(x, w, T, H, E, off, logits, s);
+    return launch_t<TA, 2, 2, 64>(x, w, T, H, E, off, logits, s);
 }
 
 }  // namespace
@@ -240,17 +260,8 @@ hipError_t launch_t(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, c
 hipError_t launch_router(const void* x, const void* w, int32_t act, int64_t T, int32_t H, int32_t E,
                          const float* offset, float* logits, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    // few tokens: one output per lane (GEMV shape); many: 4 x 4 register tiles (64 x 64 per workgroup)
-    if (act == MOE_BF16) {
-        const bf16_t* xb = (const bf16_t*)x;
-        const bf16_t* wb = (const bf16_t*)w;
-        if (T <= 512) return launch_gemv<bf16_t>(xb, wb, T, H, E, offset, logits, s);
-        return launch_t<bf16_t, 4, 4>(xb, wb, T, H, E, offset, logits, s);
-    }
-    const float* xf = (const float*)x;
-    const float* wf = (const float*)w;
-    if (T <= 512) return launch_gemv<float>(xf, wf, T, H, E, offset, logits, s);
-    return launch_t<float, 4, 4>(xf, wf, T, H, E, offset, logits, s);
+    if (act == MOE_BF16) return route_shape<bf16_t>((const bf16_t*)x, (const bf16_t*)w, T, H, E, offset, logits, s);
+    return route_shape<float>((const float*)x, (const float*)w, T, H, E, offset, logits, s);
 }
 
 }  // namespace dsmoe

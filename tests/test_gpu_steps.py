@@ -21,6 +21,11 @@ ROUTER_SHAPES = [
     (37, 200, 96, "f32"),        # ragged everywhere, partial k chunk
     (2049, 96, 1000, "bf16"),    # many experts, ragged tiles
     (1, 7168, 256, "bf16"),
+    (2048, 7168, 256, "bf16"),   # 2x4 register tiles, 64-k chunks
+    (2500, 136, 256, "f32"),     # 2x4, partial last chunk
+    (1000, 7168, 256, "bf16"),   # 2x2 register tiles, ragged tokens
+    (700, 200, 96, "f32"),       # 2x2, partial last chunk, ragged experts
+    (3000, 7168, 1, "bf16"),     # one expert (the shared-expert gate): GEMV at many tokens
 ]
 
 
