@@ -160,7 +160,42 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
 // row of x and the (wave-uniform) expert row in chunks of 32 k, kept in a ring of four register
 // buffers so that three chunks of loads are in flight while the current one is multiplied.
 // One accumulator per lane, k ascending.  grid: x = E, y = ceil(T / 64).
+//
+// The ring looks only 1.5 cache lines ahead, too little to hide HBM latency when x and the
+// expert row are not in cache (as in a layer, after the previous layer's weights have streamed
+// through).  So each wave first touches, with loads spread over its lanes, its whole expert row
+// (16 loads of 1 KB) and one slice of the 64 token rows: waves of one block that share an XCD
+// (expert ids congruent mod 8, with E a multiple of 8) split those rows between them.  The
+// values are discarded; the ring then hits in cache.
 constexpr int GV_CK = 32;
+
+template <typename TA>
+__device__ __forceinline__ uint32_t warm_rows(const TA* x, const TA* wr, int64_t T, int32_t H, int32_t E,
+                                              int32_t e, int lane) {
+    uint32_t sink = 0;
+    if (H % 8 != 0 || E < 64 || (E & 7) != 0) return sink;  // 16-byte aligned rows; 8+ waves per XCD
+    const int64_t wbytes = (int64_t)H * sizeof(TA);
+    const char* wb = (const char*)wr;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t o = (int64_t)i * 1024 + lane * 16;
+        if (o + 16 <= wbytes) sink ^= (*(const u32x4*)(wb + o))[0];
+    }
+    const int64_t t0 = (int64_t)blockIdx.y * 64;
+    const int64_t rows = T - t0 < 64 ? T - t0 : 64;
+    const int64_t xbytes = rows * H * (int64_t)sizeof(TA);  // the block's rows are contiguous
+    const int64_t lines = (xbytes + 127) / 128;
+    const int32_t q = E >> 3;                                // waves of this block on one XCD
+    const int64_t per = (lines + q - 1) / q;
+    const int64_t l0 = (int64_t)(e >> 3) * per;
+    const char* xb = (const char*)(x + t0 * H);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t j = i * 64 + lane, l = l0 + j;
+        if (j < per && l * 128 + 4 <= xbytes) sink ^= *(const uint32_t*)(xb + l * 128);
+    }
+    return sink;
+}
 
 template <typename TA>
 __device__ __forceinline__ void fma_chunk(const u32x4 (&xq)[GV_CK * sizeof(TA) / 16],
@@ -194,6 +229,7 @@ __global__ __launch_bounds__(64) void router_gemv(const TA* __restrict__ x, cons
     const int32_t e = blockIdx.x;
     const TA* xr = x + (t < T ? t : T - 1) * H;
     const TA* wr = w + (int64_t)e * H;
+    const uint32_t sink = warm_rows<TA>(x, wr, T, H, E, e, lane);
     float acc = 0.0f;
     const int nch = H / GV_CK;
     if (H % GV_CK == 0) {
@@ -219,6 +255,7 @@ __global__ __launch_bounds__(64) void router_gemv(const TA* __restrict__ x, cons
     } else {
         for (int32_t k = 0; k < H; ++k) acc = __builtin_fmaf(ld_act(xr, k), ld_act(wr, k), acc);
     }
+    asm volatile("" ::"v"(sink));  // keeps the warming loads
     if (t < T) {
         float v = acc;
         if (off) v = v + off[e];
