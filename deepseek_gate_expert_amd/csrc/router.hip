@@ -22,43 +22,48 @@ __device__ __forceinline__ float ld_act<float>(const float* p, int64_t i) { retu
 template <>
 __device__ __forceinline__ float ld_act<bf16_t>(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 
-// 8 consecutive activations as fp32 (16- or 32-byte vector loads)
+// 8 consecutive activations as loaded (16 or 32 bytes), widened to fp32 only when staged: a
+// conversion right after the load would make the load's wait come first, and the staging
+// loads would then no longer run ahead of the multiply.
 template <typename TA>
-__device__ __forceinline__ void ld8(const TA* p, float (&v)[8]);
-template <>
-__device__ __forceinline__ void ld8<bf16_t>(const bf16_t* p, float (&v)[8]) {
-    const u32x4 q = *(const u32x4*)p;
+struct Raw8 {
+    u32x4 q[sizeof(TA) / 2];
+};
+
+// elements [i, i + 8) of row `row` (length H), zero past the end of the row
+template <typename TA>
+__device__ __forceinline__ void raw8_load(const TA* row, int32_t i, int32_t H, bool vec, Raw8<TA>& r) {
+    if (vec && i + 8 <= H) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(q[i] << 16);
-        v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+        for (int v = 0; v < (int)sizeof(TA) / 2; ++v) r.q[v] = *(const u32x4*)(row + i + v * (16 / (int)sizeof(TA)));
+        return;
     }
-}
-template <>
-__device__ __forceinline__ void ld8<float>(const float* p, float (&v)[8]) {
-    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+    if constexpr (sizeof(TA) == 2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[i] = a[i];
-        v[4 + i] = b[i];
+        for (int m = 0; m < 4; ++m) {
+            const uint32_t lo = i + 2 * m < H ? row[i + 2 * m] : 0u, hi = i + 2 * m + 1 < H ? row[i + 2 * m + 1] : 0u;
+            r.q[0][m] = lo | (hi << 16);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r.q[j >> 2][j & 3] = i + j < H ? __float_as_uint(row[i + j]) : 0u;
     }
 }
 
-// 8 activations starting at element i of row `row` (length H), zero past the end of the row
+// element j of a Raw8 as fp32 (exact)
 template <typename TA>
-__device__ __forceinline__ void ld8_row(const TA* row, int32_t i, int32_t H, bool vec, float (&v)[8]) {
-    if (vec && i + 8 <= H) {
-        ld8<TA>(row + i, v);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (i + j < H) ? ld_act(row, i + j) : 0.0f;
-    }
+__device__ __forceinline__ float raw8_at(const Raw8<TA>& r, int j) {
+    if constexpr (sizeof(TA) == 2) return __uint_as_float((j & 1) ? (r.q[0][j >> 1] & 0xffff0000u) : (r.q[0][j >> 1] << 16));
+    else return __uint_as_float(r.q[j >> 2][j & 3]);
 }
 
 // Many tokens: 256 threads, MT x NT register tile per thread (BM = 16 MT tokens x BN = 16 NT
-// experts per workgroup), k chunks of KC staged in LDS as fp32 (k-major), double buffered: the
-// next chunk's global loads are in flight while the current chunk is multiplied.  Full chunks
-// run a fully unrolled k loop, so the LDS reads of later k steps issue ahead of the FMAs.
+// experts per workgroup), k chunks of KC staged in LDS as fp32 (k-major), double buffered.  The
+// global loads run RD chunks ahead in a ring of raw registers, so with x coming from HBM (as in
+// a layer) their latency stays hidden.  Full chunks run a fully unrolled k loop, so the LDS
+// reads of later k steps issue ahead of the FMAs.
+constexpr int RD = 3;
+
 template <typename TA, int MT, int NT, int KC>
 __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, const TA* __restrict__ w,
                                                      const float* __restrict__ off, float* __restrict__ logits,
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
         wrow[i] = w + (int64_t)(e < E ? e : E - 1) * H;
     }
     const int kq = (tid % LPR) * 8;
-    float xv[XL][8], wv[WL][8];
+    Raw8<TA> xq[RD][XL], wq[RD][WL];
 
     float acc[MT][NT];
 #pragma unroll
@@ -98,47 +103,51 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
         for (int j = 0; j < NT; ++j) acc[i][j] = 0.0f;
 
     const int nch = (H + KC - 1) / KC;
+    auto load = [&](int u, int c) {
 #pragma unroll
-    for (int i = 0; i < XL; ++i) ld8_row(xrow[i], kq, H, vec, xv[i]);
+        for (int i = 0; i < XL; ++i) raw8_load(xrow[i], c * KC + kq, H, vec, xq[u][i]);
 #pragma unroll
-    for (int i = 0; i < WL; ++i) ld8_row(wrow[i], kq, H, vec, wv[i]);
-    for (int c = 0; c < nch; ++c) {
-        const int b = c & 1;
+        for (int i = 0; i < WL; ++i) raw8_load(wrow[i], c * KC + kq, H, vec, wq[u][i]);
+    };
 #pragma unroll
-        for (int i = 0; i < XL; ++i)
+    for (int u = 0; u < RD; ++u)
+        if (u < nch) load(u, u);
+    for (int c0 = 0; c0 < nch; c0 += RD) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xs[b][kq + j][(tid + 256 * i) / LPR] = xv[i][j];
+        for (int u = 0; u < RD; ++u) {  // chunk c lives in ring slot c % RD
+            const int c = c0 + u;
+            if (c >= nch) break;
+            const int b = c & 1;
 #pragma unroll
-        for (int i = 0; i < WL; ++i)
+            for (int i = 0; i < XL; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ws[b][kq + j][(tid + 256 * i) / LPR] = wv[i][j];
-        __syncthreads();
-        if (c + 1 < nch) {
-            const int32_t kn = (c + 1) * KC + kq;
+                for (int j = 0; j < 8; ++j) xs[b][kq + j][(tid + 256 * i) / LPR] = raw8_at(xq[u][i], j);
 #pragma unroll
-            for (int i = 0; i < XL; ++i) ld8_row(xrow[i], kn, H, vec, xv[i]);
+            for (int i = 0; i < WL; ++i)
 #pragma unroll
-            for (int i = 0; i < WL; ++i) ld8_row(wrow[i], kn, H, vec, wv[i]);
+                for (int j = 0; j < 8; ++j) ws[b][kq + j][(tid + 256 * i) / LPR] = raw8_at(wq[u][i], j);
+            __syncthreads();
+            if (c + RD < nch) load(u, c + RD);
+            auto step = [&](int k) {
+                float a[MT], bb[NT];
+#pragma unroll
+                for (int i = 0; i < MT; ++i) a[i] = xs[b][k][ty * MT + i];
+#pragma unroll
+                for (int j = 0; j < NT; ++j) bb[j] = ws[b][k][tx * NT + j];
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
+            };
+            const int kc = min(KC, H - c * KC);  // the zero tail of the last chunk is never used
+            if (kc == KC) {
+#pragma unroll
+                for (int k = 0; k < KC; ++k) step(k);
+            } else {
+                for (int k = 0; k < kc; ++k) step(k);
+            }
+            // buffer b is rewritten two chunks later, after the next chunk's barrier
         }
-        auto step = [&](int k) {
-            float a[MT], bb[NT];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) a[i] = xs[b][k][ty * MT + i];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) bb[j] = ws[b][k][tx * NT + j];
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
-        };
-        const int kc = min(KC, H - c * KC);  // the zero tail of the last chunk is never used
-        if (kc == KC) {
-#pragma unroll
-            for (int k = 0; k < KC; ++k) step(k);
-        } else {
-            for (int k = 0; k < kc; ++k) step(k);
-        }
-        // buffer b is rewritten two chunks later, after the next iteration's barrier
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
