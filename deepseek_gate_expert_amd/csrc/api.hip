@@ -48,9 +48,10 @@ struct TilePlan {
     int32_t max_tiles;  // bound on the tile list (for the smaller of the two heights)
 };
 
-// Shapes-only decision (no device reads): tiles of 256 rows when the average group is large
-// (bf16 weights only: the 4-bit and fp8 kernel dequantises its operands in registers and
-// runs 128-row tiles).
+// Shapes-only decision (no device reads).  bf16 weights: tiles of 256 rows when the average
+// group is large, else 128.  4-bit and fp8 weights: the height of their kernel (256 rows for
+// 4-bit, 128 for fp8), each tile computed at its real height rounded up to 64 rows; 4-bit tiles
+// need the large LDS ring, without which such layers stream every group.
 TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     TilePlan p{false, 128, 128, 0};
     if (d->act_dtype != MOE_BF16 || d->T <= STREAM_MAX_ROWS) return p;
@@ -61,9 +62,11 @@ TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     if (d->T * (int64_t)d->H >= lim || rows * ldh >= lim || (int64_t)d->I * d->H >= lim ||
         (int64_t)d->I_shared * d->H >= lim)
         return p;
+    const bool quant = d->expert_dtype != MOE_BF16;
+    if (quant && tiled_quant_bm(d->expert_dtype) > (allow256 ? 256 : 128)) return p;
     p.on = true;
     const int64_t avg = d->T * d->route.top_k / d->E;
-    p.BM = (allow256 && avg >= 192 && d->expert_dtype == MOE_BF16) ? 256 : 128;
+    p.BM = quant ? tiled_quant_bm(d->expert_dtype) : (allow256 && avg >= 192) ? 256 : 128;
     // bf16 layers run the shared expert in the routed groups' launch; quantised layers give its
     // bf16 weights a launch of their own, with 256-row tiles once it has that many rows
     p.BMs = d->expert_dtype == MOE_BF16 ? p.BM : (allow256 && d->T >= 256 ? 256 : 128);

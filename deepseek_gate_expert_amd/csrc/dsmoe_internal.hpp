@@ -109,6 +109,8 @@ hipError_t launch_gemm2_f32(const GroupedArgs& a, hipStream_t s);
 // tiled grouped GEMMs (groups with more than min_rows rows; tile list built on the device)
 int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM);
 int32_t tiled_lds_bytes(int32_t BM);
+// tile height of the quantised tiled kernels for expert dtype wdt (MOE_Q4G64 or MOE_FP8)
+int32_t tiled_quant_bm(int32_t wdt);
 hipError_t configure_tiled_kernels();
 // tile list: routed groups in tiles of BM rows, the shared expert (group E) in tiles of BMs rows
 hipError_t launch_tiles(const GroupedArgs& a, int32_t BM, int32_t BMs, int32_t min_rows, int32_t* tile_count,

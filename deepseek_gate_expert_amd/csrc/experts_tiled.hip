@@ -339,9 +339,11 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 
 
 // ---------------------------------------------------------------------------------------------
-// Quantised weights, tiles of 128 rows: 4-bit (affine, groups of 64 along the reduction axis)
-// or fp8 (OCP E4M3 codes, one fp32 scale per 128 x 128 block).  Same tile shape and tile list
-// as gemm_dma.  Every operand of a 64-k stage -- the activation rows, the weight codes and the
+// Quantised weights: 4-bit (affine, groups of 64 along the reduction axis; tiles of 256 rows)
+// or fp8 (OCP E4M3 codes, one fp32 scale per 128 x 128 block; tiles of 128 rows), 256 weight
+// rows per tile, same tile list as gemm_dma.  A tile computes only its real rows rounded up to
+// 64 (a variant per height), while its weights are staged and dequantised once whatever its
+// height.  Every operand of a 64-k stage -- the activation rows, the weight codes and the
 // scales (and 4-bit offsets) -- enters LDS by DMA, in a ring of stages (three for 4-bit, two
 // for fp8: stages up to kt+NS-1 in flight while kt is computed).  With no register loads in the loop the compiler inserts
 // no waits of its own: the only waits are the explicit count + barrier per stage.  (Loading the
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 // before each use of them, which exposed the full memory latency once per stage.)
 // The dequantisation -- bf16(s*q + b), resp. bf16(value * scale) -- runs on the vector ALU
 // beside the matrix cores, one k16 step ahead of the MFMAs that consume it; to keep it at one
-// pass per weight the four waves split the tile by columns (1 x 4): wave w owns all 128 rows
+// pass per weight the four waves split the tile by columns (1 x 4): wave w owns all rows
 // and, for GEMM-1, the gate and up rows of output columns [32 w, 32 w + 32), for GEMM-2 the 64
 // columns [64 w, 64 w + 64).  Wave w also fetches those 64 weight rows' codes and scales.
 // Within a stage the k chunks are taken in the order 4h + s (lane half h, step s) for both
@@ -368,12 +370,15 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 enum { WQ_Q4 = 0, WQ_F8 = 1 };
 
 namespace wq {
-constexpr int BM = 128;
-constexpr int A_BYTES = BM * dma::ROWB;        // activations of one stage
+// rows of the tile list's tiles: 256 for 4-bit (one workgroup per CU; its dequantisation is the
+// costlier one, so halving it per row pays for the lost second workgroup), 128 for fp8 (two
+// workgroups of 66 KB share a CU)
+constexpr int bm(int wqt) { return wqt == WQ_F8 ? 128 : 256; }
 template <int WQ>
 struct Fmt {
-    // ring depth: three stages for 4-bit (two workgroups of 78 KB still share a CU), two for
-    // fp8 (so that two workgroups of 66 KB fit; three stages would hold one per CU)
+    static constexpr int BM = bm(WQ);
+    static constexpr int A_BYTES = BM * dma::ROWB;              // activation slot of one stage
+    // ring depth: three stages for 4-bit (126 KB), two for fp8 (66 KB)
     static constexpr int NS = WQ == WQ_F8 ? 2 : 3;
     static constexpr int CB = WQ == WQ_F8 ? 64 : 32;            // code bytes per weight row per stage
     static constexpr int ROWS_PER_DMA = 1024 / CB;              // weight rows per DMA instruction
@@ -382,7 +387,6 @@ struct Fmt {
     static constexpr int C_BYTES = 256 * CB;
     static constexpr int S_BYTES = 1024 * S_DMA;
     static constexpr int STAGE = A_BYTES + C_BYTES + S_BYTES;
-    static constexpr int D = A_BYTES / 1024 / 4 + C_DMA + S_DMA;  // DMAs per wave per stage
 };
 constexpr int ring_bytes(int wqt) {
     return wqt == WQ_F8 ? Fmt<WQ_F8>::NS * Fmt<WQ_F8>::STAGE : Fmt<WQ_Q4>::NS * Fmt<WQ_Q4>::STAGE;
@@ -409,30 +413,24 @@ struct BStage<WQ_F8> {
     }
 };
 
-template <int WQ, bool SWIGLU>
-__global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
+// The computed rows of one tile: MT blocks of 32 (the tile's rows rounded up to a multiple of 64).
+// Only those rows are staged and multiplied; the weights' codes and scales are staged and
+// dequantised once per tile whatever its height, so a group of up to 256 rows pays for its
+// dequantisation once.
+template <int WQ, bool SWIGLU, int MT>
+__device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t g, int32_t m0, int32_t r0,
+                                        int32_t cnt, int32_t n0) {
     using namespace dma;
     using F = wq::Fmt<WQ>;
     constexpr int NS = F::NS;
-    constexpr int BM = wq::BM;
-    constexpr int MT = BM / 32;                // 32-row blocks per wave (all rows of the tile)
-    constexpr int A_BYTES = wq::A_BYTES;
-    constexpr int A_DMA = A_BYTES / 1024 / 4;  // activation DMAs per wave per stage
-    constexpr int D = F::D;
+    constexpr int A_DMA = MT;                  // activation DMAs per wave per stage: 32 MT rows of 128 bytes
+    constexpr int D = A_DMA + F::C_DMA + F::S_DMA;
     static_assert(NS >= 2 && NS * F::STAGE <= LDS_MAX, "ring depth / size");
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-
+    static_assert(MT >= 1 && MT * 32 <= F::BM, "row blocks");
+    constexpr int A_BYTES = F::A_BYTES;
     const GroupedArgs& a = ta.a;
-    int32_t tile, ct;
-    if (!map_tile(ta, tile, ct)) return;
-    const i32x4 ti = *(const i32x4*)(ta.tile_info + 4 * tile);  // group, first row, group rows
-    const int32_t g = ti[0], m0 = ti[1], r0 = ti[2], cnt = ti[3];
-    if (g < ta.g0 || g >= ta.g1 || g >= a.E) return;  // routed groups only (the shared expert is bf16)
     const int32_t N = SWIGLU ? a.I : a.H;
     const int32_t KD = SWIGLU ? a.H : a.I;
-    constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
-    const int32_t n0 = ct * OUT_COLS;
-    if (n0 >= N) return;
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5;
 
@@ -565,6 +563,9 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     // the MFMAs of step `buf`, with the next step's operand work (issued just before, in program
     // order) spread between them: its LDS reads first, then a few dequantisation instructions
     // after each MFMA, so the vector ALU runs while the matrix core does
+    // the next step's dequantisation (about 40 vector instructions for fp8, 56 for 4-bit) spread
+    // evenly over this step's 2 MT MFMAs
+    constexpr int VPM = ((WQ == WQ_F8 ? 40 : 56) + 2 * MT - 1) / (2 * MT);
     auto mfma_step = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
 #pragma unroll
         for (int q = 0; q < 2 * MT; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, WQ == WQ_F8 ? 5 : 7, 0);  // then vector ALU work
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // then vector ALU work
         }
     };
     // One stage.  At the barrier everything but the newest (NS-2) D operations (stage kt+NS-1,
@@ -632,6 +633,35 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
                     ((bf16_t*)a.o)[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[i][j][v]);
             }
         }
+}
+
+template <int WQ, bool SWIGLU>
+__global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const GroupedArgs& a = ta.a;
+    int32_t tile, ct;
+    if (!map_tile(ta, tile, ct)) return;
+    const i32x4 ti = *(const i32x4*)(ta.tile_info + 4 * tile);  // group, first row, group rows
+    const int32_t g = ti[0], m0 = ti[1], r0 = ti[2], cnt = ti[3];
+    if (g < ta.g0 || g >= ta.g1 || g >= a.E) return;  // routed groups only (the shared expert is bf16)
+    const int32_t N = SWIGLU ? a.I : a.H;
+    constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
+    const int32_t n0 = ct * OUT_COLS;
+    if (n0 >= N) return;
+    // rows of this tile, rounded up to 64: selects the variant (uniform over the workgroup)
+    constexpr int BM = wq::bm(WQ);
+    const int32_t rows = min(cnt - m0, (int32_t)BM);
+    const int32_t q64 = __builtin_amdgcn_readfirstlane((rows + 63) >> 6);
+    if constexpr (BM == 256) {
+        if (q64 >= 4) wq_tile<WQ, SWIGLU, 8>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q64 == 3) wq_tile<WQ, SWIGLU, 6>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q64 == 2) wq_tile<WQ, SWIGLU, 4>(ta, smem, g, m0, r0, cnt, n0);
+        else wq_tile<WQ, SWIGLU, 2>(ta, smem, g, m0, r0, cnt, n0);
+    } else {
+        static_assert(BM == 128, "tile height");
+        if (q64 >= 2) wq_tile<WQ, SWIGLU, 4>(ta, smem, g, m0, r0, cnt, n0);
+        else wq_tile<WQ, SWIGLU, 2>(ta, smem, g, m0, r0, cnt, n0);
+    }
 }
 
 // Tile list (offsets is read only for routed groups: it may be NULL when E == 0): every group in
@@ -705,9 +735,13 @@ int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM) {
 
 // largest dynamic LDS any tiled kernel of this tile height uses
 int32_t tiled_lds_bytes(int32_t BM) {
-    const int32_t dma_ring = dma::ring_bytes(BM), wq_ring = max(wq::ring_bytes(WQ_F8), wq::ring_bytes(WQ_Q4));
-    return BM == wq::BM && wq_ring > dma_ring ? wq_ring : dma_ring;
+    int32_t r = dma::ring_bytes(BM);
+    if (BM == wq::bm(WQ_F8)) r = max(r, wq::ring_bytes(WQ_F8));
+    if (BM == wq::bm(WQ_Q4)) r = max(r, wq::ring_bytes(WQ_Q4));
+    return r;
 }
+
+int32_t tiled_quant_bm(int32_t wdt) { return wq::bm(wdt == MOE_FP8 ? WQ_F8 : WQ_Q4); }
 
 hipError_t configure_tiled_kernels() {
     // allow the large dynamic LDS allocations (up to 128 KB) of the tiled kernels
@@ -717,7 +751,7 @@ hipError_t configure_tiled_kernels() {
         (const void*)gemm_dma_wq<WQ_Q4, true>,      (const void*)gemm_dma_wq<WQ_Q4, false>,
         (const void*)gemm_dma_wq<WQ_F8, true>,      (const void*)gemm_dma_wq<WQ_F8, false>,
     };
-    const int bms[] = {256, 256, 128, 128, 128, 128, 128, 128};
+    const int bms[] = {256, 256, 128, 128, wq::bm(WQ_Q4), wq::bm(WQ_Q4), wq::bm(WQ_F8), wq::bm(WQ_F8)};
     for (int i = 0; i < 8; ++i) {
         hipError_t e = hipFuncSetAttribute(ks[i], hipFuncAttributeMaxDynamicSharedMemorySize, tiled_lds_bytes(bms[i]));
         if (e != hipSuccess) return e;
@@ -749,8 +783,8 @@ hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32
         if (BM == 256) return gemm1 ? launch_dma_t<256, true>(ta, s) : launch_dma_t<256, false>(ta, s);
         return gemm1 ? launch_dma_t<128, true>(ta, s) : launch_dma_t<128, false>(ta, s);
     }
-    // quantised layers always use tiles of 128 rows (plan_tiles)
-    if (BM != 128) return hipErrorInvalidValue;
+    // quantised layers use the tile height of their format (plan_tiles)
+    if (BM != tiled_quant_bm(wdt)) return hipErrorInvalidValue;
     if (wdt == MOE_FP8) return gemm1 ? launch_dma_wq_t<WQ_F8, true>(ta, s) : launch_dma_wq_t<WQ_F8, false>(ta, s);
     if (wdt == MOE_Q4G64) return gemm1 ? launch_dma_wq_t<WQ_Q4, true>(ta, s) : launch_dma_wq_t<WQ_Q4, false>(ta, s);
     return hipErrorInvalidValue;
