@@ -19,6 +19,7 @@
 // MFMA 32x32x16 bf16 layout: lane l supplies row/column (l % 32) and the 8 k values of chunk
 // (l / 32) of each 16-k step; result element v of lane l is row 8*(v/4) + 4*(l/32) + v%4,
 // column l % 32.  Which 8 k values a chunk holds is free as long as both operands agree.
+#include <type_traits>
 #include "dsmoe_internal.hpp"
 
 namespace dsmoe {
@@ -290,48 +291,72 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
     // sits before the last step of stage kt; once every wave has passed it, the fragments of
     // stage kt are all in registers, so its slot is refilled with stage kt+NST right away and
     // those loads have the next four steps to land.
+    // A wave multiplies only its NV row blocks of 32 that hold rows of the group (the last tile of
+    // a group is ragged); NV = 0 leaves the wave to the barriers, so the other wave on its SIMD
+    // has the matrix core to itself.  Every variant passes the same barriers.
     const int nk = KD / BKD;  // >= 1
     bf16x8 fa[2][MT], fb[2][2];
-    auto read_frags = [&](int kt, int s, int buf) {
-        const char* st = smem + (kt % NST) * ST_BYTES;
-        const int c = 2 * s + (lane >> 5);
+    auto kloop = [&](auto nv_c) {
+        constexpr int NV = decltype(nv_c)::value;
+        auto read_frags = [&](int kt, int s, int buf) {
+            if constexpr (NV > 0) {
+                const char* st = smem + (kt % NST) * ST_BYTES;
+                const int c = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            fb[buf][j] = as_bf16x8(*(const u32x4*)(st + A_BYTES + off(brow[j] + (lane & 31), c)));
+                for (int j = 0; j < 2; ++j)
+                    fb[buf][j] = as_bf16x8(*(const u32x4*)(st + A_BYTES + off(brow[j] + (lane & 31), c)));
 #pragma unroll
-        for (int i = 0; i < MT; ++i) fa[buf][i] = as_bf16x8(*(const u32x4*)(st + off(wm * WM + i * 32 + (lane & 31), c)));
-    };
-    // one k16 step: its first MFMA, then (optionally) the next step's fragment reads, then the
-    // remaining MFMAs -- pinned in that order so each LDS read issues under a running MFMA
-    auto mfma_step = [&](int buf, bool then_read, int rkt, int rs, int rbuf) {
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][0], fb[buf][0], acc[0][0], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (then_read) {
-            read_frags(rkt, rs, rbuf);
-            __builtin_amdgcn_sched_group_barrier(0x100, MT + 2, 0);
+                for (int i = 0; i < NV; ++i)
+                    fa[buf][i] = as_bf16x8(*(const u32x4*)(st + off(wm * WM + i * 32 + (lane & 31), c)));
+            }
+        };
+        // one k16 step: its first MFMA, then (optionally) the next step's fragment reads, then the
+        // remaining MFMAs -- pinned in that order so each LDS read issues under a running MFMA
+        auto mfma_step = [&](int buf, bool then_read, int rkt, int rs, int rbuf) {
+            if constexpr (NV > 0) {
+                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][0], fb[buf][0], acc[0][0], 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (then_read) {
+                    read_frags(rkt, rs, rbuf);
+                    __builtin_amdgcn_sched_group_barrier(0x100, NV + 2, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        if (i | j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, NV * 2 - 1, 0);
+            }
+        };
+        const int pro = min(nk, NST);  // stages issued up front
+        for (int j = 0; j < pro; ++j) issue(j);
+        wait_stages<D>(pro - 1);
+        read_frags(0, 0, 0);
+        for (int kt = 0; kt < nk; ++kt) {
+            mfma_step(0, true, kt, 1, 1);
+            mfma_step(1, true, kt, 2, 0);
+            mfma_step(0, true, kt, 3, 1);
+            const bool next = kt + 1 < nk;
+            if (next) {
+                // issued so far: stages < min(nk, kt + NST); wait for kt+1, let the later ones fly
+                wait_stages<D>(min(nk, kt + NST) - (kt + 2));
+                if (kt + NST < nk) issue(kt + NST);
+            }
+            mfma_step(1, next, kt + 1, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                if (i | j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, MT * 2 - 1, 0);
     };
-    const int pro = min(nk, NST);  // stages issued up front
-    for (int j = 0; j < pro; ++j) issue(j);
-    wait_stages<D>(pro - 1);
-    read_frags(0, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        mfma_step(0, true, kt, 1, 1);
-        mfma_step(1, true, kt, 2, 0);
-        mfma_step(0, true, kt, 3, 1);
-        const bool next = kt + 1 < nk;
-        if (next) {
-            // issued so far: stages < min(nk, kt + NST); wait for kt+1, let the later ones fly
-            wait_stages<D>(min(nk, kt + NST) - (kt + 2));
-            if (kt + NST < nk) issue(kt + NST);
+    {
+        const int32_t rows = min(cnt - m0, (int32_t)BM) - wm * WM;  // rows of the group in this wave's half
+        const int nv = rows <= 0 ? 0 : min((rows + 31) >> 5, MT);
+        static_assert(MT == 2 || MT == 4, "row blocks per wave");
+        if (nv >= MT) kloop(std::integral_constant<int, MT>{});
+        else if (nv == 0) kloop(std::integral_constant<int, 0>{});
+        else if (nv == 1) kloop(std::integral_constant<int, 1>{});
+        else if constexpr (MT == 4) {
+            if (nv == 2) kloop(std::integral_constant<int, 2>{});
+            else kloop(std::integral_constant<int, 3>{});
         }
-        mfma_step(1, next, kt + 1, 0, 0);
     }
 
     tile_epilogue<BM, SWIGLU>(a, acc, smem, r0, cnt, m0, n0, N, wm, wn, tid);
