@@ -90,15 +90,17 @@ def gemm1_bytes(w, n_hit: int) -> float:
     return n_hit * per_expert + 2 * w.Is * w.H * act + w.T * w.H * act
 
 
-# the library computes expert groups of more than this many rows (and the shared expert, whose
-# group holds all T rows) in the MFMA-tiled kernels when T exceeds it; smaller groups are streamed
+# when T exceeds it, the library computes bf16 expert groups of more than this many rows (and the
+# shared expert, whose group holds all T rows) in the MFMA-tiled kernels and streams the smaller
+# groups; 4-bit and fp8 routed groups of every size are tiled
 STREAM_MAX_ROWS = 64
 
 
 def tiled_gemm1_flops(w, counts) -> float:
-    """Algorithmic flops of one launch of the tiled gate/up kernel: 2 (gate, up) x 2 x H x I per
-    row of every group above STREAM_MAX_ROWS rows, plus the shared expert's T rows."""
-    rows = int(counts[counts > STREAM_MAX_ROWS].sum())
+    """Algorithmic flops of the tiled gate/up launches: 2 (gate, up) x 2 x H x I per row of every
+    tiled group, plus the shared expert's T rows."""
+    lim = 0 if w.expert in ("q4", "fp8") else STREAM_MAX_ROWS
+    rows = int(counts[counts > lim].sum())
     return 4.0 * w.H * (w.I * rows + w.Is * w.T)
 
 
@@ -321,7 +323,7 @@ def main():
                     "kernel": ("gemm_dma<256, true> (tiled gate/up + SwiGLU: groups above 64 rows and the "
                                "shared expert)") if wl.expert == "bf16" else
                               (f"tiled gate/up + SwiGLU kernels: gemm_dma_wq<{wl.expert}, true> for the {wl.expert} "
-                               "routed groups above 64 rows, gemm_dma<128, true> for the bf16 shared expert")}
+                               "routed groups, gemm_dma<256, true> for the bf16 shared expert")}
             layer = layer_flops(wl) / (res["step_ms"] / 1e3) / 1e12
             roof["layer_achieved"] = layer
             roof["layer_frac"] = layer / PEAK_BF16_TFLOPS

@@ -46,6 +46,7 @@ struct TilePlan {
     int32_t BM;         // tile height of the routed groups
     int32_t BMs;        // tile height of the shared expert
     int32_t max_tiles;  // bound on the tile list (for the smaller of the two heights)
+    int32_t min_rows;   // groups with more rows than this are tiled, the others streamed
 };
 
 // Shapes-only decision (no device reads).  bf16 weights: tiles of 256 rows when the average
@@ -53,7 +54,7 @@ struct TilePlan {
 // 4-bit, 128 for fp8), each tile computed at its real height rounded up to 64 rows; 4-bit tiles
 // need the large LDS ring, without which such layers stream every group.
 TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
-    TilePlan p{false, 128, 128, 0};
+    TilePlan p{false, 128, 128, 0, STREAM_MAX_ROWS};
     if (d->act_dtype != MOE_BF16 || d->T <= STREAM_MAX_ROWS) return p;
     // the tiled kernels address activation and weight rows with 32-bit byte offsets
     const int64_t rows = d->T * d->route.top_k + d->T;
@@ -71,6 +72,10 @@ TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     // bf16 weights a launch of their own, with 256-row tiles once it has that many rows
     p.BMs = d->expert_dtype == MOE_BF16 ? p.BM : (allow256 && d->T >= 256 ? 256 : 128);
     p.max_tiles = tiled_max_tiles(d->T, d->route.top_k, d->E, p.BM < p.BMs ? p.BM : p.BMs);
+    // Quantised routed groups of any size go to the tiled kernel, whose 64-row variant moves
+    // the codes by DMA and dequantises each weight once: for small groups it outruns the
+    // streaming kernel, whose 4-bit steps are a few short loads per lane and a barrier.
+    if (quant) p.min_rows = 0;
     return p;
 }
 
@@ -445,12 +450,12 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     const int32_t gend = E + (d->I_shared > 0 ? 1 : 0);
     const bool f32 = d->act_dtype == MOE_F32;
     const bool quant = d->expert_dtype == MOE_Q4G64 || d->expert_dtype == MOE_FP8;
-    TilePlan tp{false, 128, 128, 0};
+    TilePlan tp{false, 128, 128, 0, STREAM_MAX_ROWS};
     if (!f32) {
         const int ts = tiled_state();
         if (ts != 3) tp = plan_tiles(d, ts == 1);
     }
-    a.stream_max_rows = tp.on ? STREAM_MAX_ROWS : 0x7fffffff;
+    a.stream_max_rows = tp.on ? tp.min_rows : 0x7fffffff;
     const int32_t rdt = quant ? d->expert_dtype : MOE_BF16;
     const int32_t split = quant ? E : gend;  // tiled: quantised routed groups vs the bf16 (shared) group
     // weight-streaming kernels of one expert-GEMM pass (groups of at most stream_max_rows rows);
@@ -458,6 +463,7 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     // also in quantised layers
     auto streamed = [&](bool first) -> int {
         if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));
+        if (tp.on && tp.min_rows == 0) return MOE_OK;  // every group is tiled
         return hip_rc(first ? launch_gemm1_bf16(a, 0, gend, rdt, s) : launch_gemm2_bf16(a, 0, gend, rdt, s));
     };
     // tiled kernels of one pass (the other groups)
@@ -469,7 +475,7 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
                                          tp.max_tiles, s));
         return r;
     };
-    if (tp.on && (rc = hip_rc(launch_tiles(a, tp.BM, tp.BMs, STREAM_MAX_ROWS, tile_count, tile_info, s)))) return rc;
+    if (tp.on && (rc = hip_rc(launch_tiles(a, tp.BM, tp.BMs, tp.min_rows, tile_count, tile_info, s)))) return rc;
     // With tiles on, the GEMM1 / GEMM2 stage events bracket the tiled kernels only (the
     // dominant kernels of prefill layers); the streaming kernels run right before them.
     for (int pass = 0; pass < 2; ++pass) {
