@@ -38,15 +38,22 @@ enum { WF_BF16 = 0, WF_Q4 = 1, WF_F8 = 2 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float b) {
+// Eight 4-bit codes (code i at bits 4i) -> bf16(s q + b), given s512 = 512 s.  A code q in the
+// low nibble of a byte, read as an OCP E4M3 code, has the value q * 2^-9 (a subnormal for q < 8,
+// exponent field 1 above), so one hardware E4M3 -> fp32 conversion turns two codes into exact
+// floats; 512 s * (q * 2^-9) is exactly s q, so the fma rounds s q + b once, as fma(s, q, b) would.
+// (512 s overflows only for |s| > 6.6e35.)
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s512, float b) {
     u32x4 r;
-    // codes 2j and 2j+1 are the low and high nibble of byte j: split the nibbles into bytes once,
-    // then convert each byte directly
-    const uint32_t lo4 = w & 0x0F0F0F0Fu, hi4 = (w >> 4) & 0x0F0F0F0Fu;
-    r[0] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<0>(lo4), b), __builtin_fmaf(s, cvt_ubyte<0>(hi4), b));
-    r[1] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<1>(lo4), b), __builtin_fmaf(s, cvt_ubyte<1>(hi4), b));
-    r[2] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<2>(lo4), b), __builtin_fmaf(s, cvt_ubyte<2>(hi4), b));
-    r[3] = pack_bf16x2(__builtin_fmaf(s, cvt_ubyte<3>(lo4), b), __builtin_fmaf(s, cvt_ubyte<3>(hi4), b));
+    const uint32_t lo4 = w & 0x0F0F0F0Fu, hi4 = (w >> 4) & 0x0F0F0F0Fu;  // codes 0,2,4,6 / 1,3,5,7
+    const auto e02 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo4, false);  // codes 0, 2
+    const auto e46 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo4, true);   // codes 4, 6
+    const auto e13 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi4, false);  // codes 1, 3
+    const auto e57 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi4, true);   // codes 5, 7
+    r[0] = pack_bf16x2(__builtin_fmaf(s512, e02[0], b), __builtin_fmaf(s512, e13[0], b));
+    r[1] = pack_bf16x2(__builtin_fmaf(s512, e02[1], b), __builtin_fmaf(s512, e13[1], b));
+    r[2] = pack_bf16x2(__builtin_fmaf(s512, e46[0], b), __builtin_fmaf(s512, e57[0], b));
+    r[3] = pack_bf16x2(__builtin_fmaf(s512, e46[1], b), __builtin_fmaf(s512, e57[1], b));
     return as_bf16x8(r);
 }
 
@@ -100,7 +107,7 @@ template <>
 struct WRegs<WF_Q4> {
     u32x4 q;
     bf16_t s, b;
-    __device__ __forceinline__ bf16x8 frag(int i) const { return dequant8(q[i], bf16_to_f32(s), bf16_to_f32(b)); }
+    __device__ __forceinline__ bf16x8 frag(int i) const { return dequant8(q[i], 512.0f * bf16_to_f32(s), bf16_to_f32(b)); }
 };
 template <>
 struct WRegs<WF_F8> {
