@@ -216,3 +216,51 @@ def test_layer_fp8_every_code(T):
     err = rel_l2(act_to_f64(y), y_ref)
     log(f"[fp8 codes] T={T} rel L2 {err:.3e}")
     assert err <= tol_of(w_)
+
+
+# Group sizes chosen to meet every tile-height variant: the last tile of a group holds 1..BM rows,
+# which selects how many 32-row blocks each wave of the bf16 kernel multiplies (0..4 per half of a
+# 256-row tile, 0..2 per half of a 128-row one) and which height variant of the quantised kernels
+# runs (64/128/192/256 rows for 4-bit, 64/128 for fp8); groups of at most 64 rows are streamed in
+# bf16 layers and tiled in quantised ones; two experts receive no rows.  SIZES_256 has a mean
+# group (over all 18 experts) of 192 rows, so bf16 layers use 256-row tiles; SIZES_128 a mean of
+# 133 (128-row tiles).
+SIZES_256 = [1, 33, 64, 65, 96, 0, 128, 129, 160, 161, 200, 0, 250, 256, 257, 300, 511, 849]
+SIZES_128 = [1, 40, 64, 65, 80, 0, 96, 97, 127, 128, 129, 0, 150, 200, 255, 256, 300, 412]
+
+
+def exact_group_case(sizes, K, expert):
+    """A layer whose routing puts exactly sizes[e] rows in group e: the router is the identity on
+    the first E input columns and token t carries 4.0 in the columns of its K experts (0 in the
+    other routing columns, N(0,1) elsewhere), so its K largest logits are exactly those experts."""
+    E = len(sizes)
+    TK = sum(sizes)
+    assert TK % K == 0
+    T = TK // K
+    assert max(sizes) <= T
+    w = C1.with_(T=T, H=256, E=E, K=K, G=1, TG=1, I=128, Is=64, expert=expert, planted=0)
+    slots = np.repeat(np.arange(E), sizes)          # expert of each slot, expert-major
+    chosen = slots.reshape(K, T).T                    # token t: slots t, t + T, ..., distinct experts
+    x = synth.normal_bf16(w.seed, 1, T * w.H).reshape(T, w.H)
+    x[:, :E] = 0
+    x[np.arange(T)[:, None], chosen] = synth.f32_to_bf16(np.array([4.0], np.float32))[0]
+    r = np.zeros((E, w.H), np.uint16)
+    r[np.arange(E), np.arange(E)] = synth.f32_to_bf16(np.array([1.0], np.float32))[0]
+    b = np.zeros(E, np.float32)
+    return w, r, b, x, synth.gen_expert_weights(w), synth.gen_shared(w), None
+
+
+@pytest.mark.parametrize("sizes,expert", [(SIZES_256, "bf16"), (SIZES_128, "bf16"), (SIZES_256, "q4"),
+                                          (SIZES_128, "fp8"), (SIZES_256, "fp8")],
+                         ids=["bf16_tiles256", "bf16_tiles128", "q4", "fp8", "fp8_tall_groups"])
+def test_layer_exact_group_sizes(sizes, expert):
+    w, r, b, x, ex, sh, off = exact_group_case(sizes, 4, expert)
+    log(f"[groups] {expert}: T={w.T} sizes {sizes}")
+    y, gi, gs = run_small(w, r, b, x, ex, sh, off)
+    y_ref, oi, os_, _ = oracle.forward_workload(w, x, r, b, ex, sh, offset=off,
+                                                shared_gate=synth.gen_shared_gate(w))
+    assert np.array_equal(np.bincount(oi.ravel(), minlength=w.E), np.array(sizes))
+    check_route(gi, gs, oi, os_)
+    err = rel_l2(act_to_f64(y), y_ref)
+    log(f"[groups] {expert} rel L2 {err:.3e}")
+    assert err <= tol_of(w)
