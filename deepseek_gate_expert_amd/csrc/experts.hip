@@ -304,7 +304,9 @@ __device__ __forceinline__ void stream_body(const GroupedArgs& a, int32_t g, cha
         // One full step: publish its activations, start the loads of steps s+2 (activations) and
         // s+D (weights), run its MFMAs.  Activations run two steps ahead in three LDS buffers;
         // weights run D steps ahead in D+1 rotating register sets (D = 3 for fp8, whose steps
-        // carry half the bytes of bf16 ones, so more of them must be in flight; else 2).  Per wave
+        // carry half the bytes of bf16 ones, so more of them must be in flight, and for the bf16
+        // down projection, whose reduction of I is only a few steps long, so its pipeline fill
+        // weighs more; else 2).  Per wave
         // the issue order is A(s+2), W(s+D) during step s.  At the top of step s, A(s) and W(s)
         // must have landed; what may stay in flight is everything issued after them -- for
         // D = 2: A(s+1), W(s+1); for D > 2 (W(s) is older than A(s)): W(s+D-2), A(s+1),
@@ -313,7 +315,7 @@ __device__ __forceinline__ void stream_body(const GroupedArgs& a, int32_t g, cha
         // load sequence on every path the compiler's own waits for the weight registers stay
         // exact rather than falling back to waiting for everything.
         constexpr int WL = NW * (WF == WF_BF16 ? 4 : 3);  // vector-memory operations of one load_full
-        constexpr int D = WF == WF_F8 ? 3 : 2;
+        constexpr int D = (WF == WF_F8 || (WF == WF_BF16 && !G1)) ? 3 : 2;
         constexpr int NWS = D + 1;
         constexpr int LATER_COPY = D == 2 ? 4 + WL : 4 + 2 * WL;  // waves that copy activation rows
         constexpr int LATER_NOCOPY = (D - 1) * WL;                // waves that do not
