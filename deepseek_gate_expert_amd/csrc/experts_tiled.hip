@@ -374,7 +374,7 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 // Quantised weights: 4-bit (affine, groups of 64 along the reduction axis; tiles of 256 rows)
 // or fp8 (OCP E4M3 codes, one fp32 scale per 128 x 128 block; tiles of 128 rows), 256 weight
 // rows per tile, same tile list as gemm_dma.  A tile computes only its real rows rounded up to
-// 64 (a variant per height), while its weights are staged and dequantised once whatever its
+// 32 (a variant per height), while its weights are staged and dequantised once whatever its
 // height.  Every operand of a 64-k stage -- the activation rows, the weight codes and the
 // scales (and 4-bit offsets) -- enters LDS by DMA, in a ring of stages (three for 4-bit, two
 // for fp8: stages up to kt+NS-1 in flight while kt is computed).  With no register loads in the loop the compiler inserts
@@ -445,7 +445,7 @@ struct BStage<WQ_F8> {
     }
 };
 
-// The computed rows of one tile: MT blocks of 32 (the tile's rows rounded up to a multiple of 64).
+// The computed rows of one tile: MT blocks of 32 (the tile's rows rounded up to a multiple of 32).
 // Only those rows are staged and multiplied; the weights' codes and scales are staged and
 // dequantised once per tile whatever its height, so a group of up to 256 rows pays for its
 // dequantisation once.
@@ -680,19 +680,25 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
     const int32_t n0 = ct * OUT_COLS;
     if (n0 >= N) return;
-    // rows of this tile, rounded up to 64: selects the variant (uniform over the workgroup)
+    // rows of this tile, rounded up to 32: selects the variant (uniform over the workgroup)
     constexpr int BM = wq::bm(WQ);
     const int32_t rows = min(cnt - m0, (int32_t)BM);
-    const int32_t q64 = __builtin_amdgcn_readfirstlane((rows + 63) >> 6);
+    const int32_t q32 = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
     if constexpr (BM == 256) {
-        if (q64 >= 4) wq_tile<WQ, SWIGLU, 8>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q64 == 3) wq_tile<WQ, SWIGLU, 6>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q64 == 2) wq_tile<WQ, SWIGLU, 4>(ta, smem, g, m0, r0, cnt, n0);
-        else wq_tile<WQ, SWIGLU, 2>(ta, smem, g, m0, r0, cnt, n0);
+        if (q32 >= 8) wq_tile<WQ, SWIGLU, 8>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 7) wq_tile<WQ, SWIGLU, 7>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 6) wq_tile<WQ, SWIGLU, 6>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 5) wq_tile<WQ, SWIGLU, 5>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 4) wq_tile<WQ, SWIGLU, 4>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 3) wq_tile<WQ, SWIGLU, 3>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 2) wq_tile<WQ, SWIGLU, 2>(ta, smem, g, m0, r0, cnt, n0);
+        else wq_tile<WQ, SWIGLU, 1>(ta, smem, g, m0, r0, cnt, n0);
     } else {
         static_assert(BM == 128, "tile height");
-        if (q64 >= 2) wq_tile<WQ, SWIGLU, 4>(ta, smem, g, m0, r0, cnt, n0);
-        else wq_tile<WQ, SWIGLU, 2>(ta, smem, g, m0, r0, cnt, n0);
+        if (q32 >= 4) wq_tile<WQ, SWIGLU, 4>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 3) wq_tile<WQ, SWIGLU, 3>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 2) wq_tile<WQ, SWIGLU, 2>(ta, smem, g, m0, r0, cnt, n0);
+        else wq_tile<WQ, SWIGLU, 1>(ta, smem, g, m0, r0, cnt, n0);
     }
 }
 
