@@ -48,17 +48,6 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(bf16_t, b);
 }
 
-// byte N of x as fp32 (v_cvt_f32_ubyteN; the compiler otherwise extracts the byte first)
-template <int N>
-__device__ __forceinline__ float cvt_ubyte(uint32_t x) {
-    float f;
-    if constexpr (N == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(x));
-    else if constexpr (N == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
-    else if constexpr (N == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(x));
-    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(x));
-    return f;
-}
-
 // two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
