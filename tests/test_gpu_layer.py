@@ -264,3 +264,7 @@ def test_layer_exact_group_sizes(sizes, expert):
     err = rel_l2(act_to_f64(y), y_ref)
     log(f"[groups] {expert} rel L2 {err:.3e}")
     assert err <= tol_of(w)
+    # the tiled paths sum in a fixed order with no atomics: a second call gives the same bits
+    y2, gi2, gs2 = run_small(w, r, b, x, ex, sh, off)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert np.array_equal(gi, gi2) and np.array_equal(gs.view(np.uint32), gs2.view(np.uint32))
