@@ -5,12 +5,14 @@
 // into the gate/up GEMM's epilogue), organised for the prefill regime where a group holds
 // hundreds or thousands of rows and the work is bound by MFMA throughput:
 //
-//   * a workgroup (4 waves) computes a BM x 256 tile: BM rows of one group against 256 rows of
-//     weights -- for GEMM-1 the gate and up rows of the same 128 output columns, for GEMM-2 256
-//     rows of W_down -- with v_mfma_f32_32x32x16_bf16 and fp32 accumulators;
+//   * a workgroup computes a BM x 256 tile: BM rows of one group against 256 rows of weights --
+//     for GEMM-1 the gate and up rows of the same 128 output columns, for GEMM-2 256 rows of
+//     W_down -- with v_mfma_f32_32x32x16_bf16 and fp32 accumulators, multiplying only the
+//     32-row blocks that hold rows of the group;
 //   * operands reach LDS by direct-to-LDS DMA in k-stages of 64 (one 128-byte line per row),
-//     through a ring of stages, with one barrier per stage (gemm_dma); 4-bit and fp8 weights skip
-//     LDS and are dequantised in registers (gemm_dma_wq);
+//     through a ring of stages, with one barrier per stage: bf16 weights in 8-wave workgroups
+//     (gemm_dma); 4-bit and fp8 codes and scales in 4-wave workgroups that dequantise them in
+//     registers before the MFMA (gemm_dma_wq);
 //   * the list of (group, first row) tiles is built on the device from the dispatch offsets, so
 //     no count ever returns to the host; the grid is an upper bound and surplus workgroups exit;
 //   * workgroup ids are remapped so that the workgroups an XCD receives (ids congruent mod 8)

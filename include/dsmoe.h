@@ -196,11 +196,11 @@ int moe_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* 
  *                                                      that goes through silu)
  * Steps, all on `stream`: router logits (as moe_router_logits) -> gate (as moe_route_deepseek,
  * or moe_route_softmax when route_kind is MOE_ROUTE_SOFTMAX) -> dispatch (as moe_dispatch) ->
- * grouped gate/up GEMM with SwiGLU in the epilogue -> grouped down GEMM -> combine.  For bf16,
- * 4-bit and fp8 layers with T > 64, each grouped GEMM is split by group size: weight streaming for
- * the expert groups of at most 64 rows, MFMA tiles for the larger groups and the shared expert
- * (one tiled launch for bf16 layers; in 4-bit and fp8 layers the quantised routed groups and the
- * bf16 shared expert have a tiled launch each).
+ * grouped gate/up GEMM with SwiGLU in the epilogue -> grouped down GEMM -> combine.  For bf16
+ * layers with T > 64, each grouped GEMM is split by group size: weight streaming for the expert
+ * groups of at most 64 rows, MFMA tiles (one launch) for the larger groups and the shared
+ * expert.  For 4-bit and fp8 layers with T > 64, every quantised routed group is tiled, in a
+ * launch of its own beside the bf16 shared expert's.  With T <= 64 every group is streamed.
  * The combine adds, per token and output element, the (gated) shared expert's output and then
  * the K weighted expert outputs in j order in fp32, with no atomics.
  * Precision: bf16 layers run bf16 MFMA with fp32 accumulation; the SwiGLU intermediate and the
