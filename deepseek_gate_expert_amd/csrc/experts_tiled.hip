@@ -81,10 +81,12 @@ struct TileArgs {
 };
 
 // Workgroup -> (tile, column tile).  The logical space holds tile_count * col_tiles items in
-// bands of 4 column tiles: items of one band walk the row tiles with the column fastest, so the
+// bands of CB column tiles (4 for the bf16 kernel, 2 for the quantised ones, measured): items of
+// one band walk the row tiles with the column fastest, so the
 // workgroups running at once share both A panels (same rows) and B panels (same group and
 // columns).  Workgroup ids congruent mod 8 land on the same XCD; each XCD takes one contiguous
 // eighth of the logical space, sized by the tile count actually built (the grid is a bound).
+template <int32_t CB>
 __device__ __forceinline__ bool map_tile(const TileArgs& ta, int32_t& tile, int32_t& ct) {
     const int32_t ntiles = ta.tile_count[0];
     const int32_t total = ntiles * ta.col_tiles;
@@ -94,7 +96,6 @@ __device__ __forceinline__ bool map_tile(const TileArgs& ta, int32_t& tile, int3
     if (pos >= per_xcd) return false;
     const int32_t l = (bid & 7) * per_xcd + pos;
     if (l >= total) return false;
-    constexpr int32_t CB = 4;
     const int32_t band = l / (ntiles * CB);
     const int32_t bw = min(CB, ta.col_tiles - band * CB);
     const int32_t rem = l - band * ntiles * CB;
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 
     const GroupedArgs& a = ta.a;
     int32_t tile, ct;
-    if (!map_tile(ta, tile, ct)) return;
+    if (!map_tile<4>(ta, tile, ct)) return;
     const i32x4 ti = *(const i32x4*)(ta.tile_info + 4 * tile);  // group, first row, group rows
     const int32_t g = ti[0], m0 = ti[1], r0 = ti[2], cnt = ti[3];
     if (g < ta.g0 || g >= ta.g1) return;
@@ -674,7 +675,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const GroupedArgs& a = ta.a;
     int32_t tile, ct;
-    if (!map_tile(ta, tile, ct)) return;
+    if (!map_tile<2>(ta, tile, ct)) return;
     const i32x4 ti = *(const i32x4*)(ta.tile_info + 4 * tile);  // group, first row, group rows
     const int32_t g = ti[0], m0 = ti[1], r0 = ti[2], cnt = ti[3];
     if (g < ta.g0 || g >= ta.g1 || g >= a.E) return;  // routed groups only (the shared expert is bf16)
