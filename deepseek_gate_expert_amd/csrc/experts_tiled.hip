@@ -598,8 +598,8 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
         for (int j = 0; j < 2; ++j) fb[buf][j] = as_bf16x8(bs.deq(j, s));
     };
     // the MFMAs of step `buf`, with the next step's operand work (issued just before, in program
-    // order) spread between them: its LDS reads first, then a few dequantisation instructions
-    // after each MFMA, so the vector ALU runs while the matrix core does
+    // order) spread between them: after each MFMA one of its LDS reads (while they last) and a
+    // few dequantisation instructions, so the LDS and the vector ALU run while the matrix core does
     // the next step's dequantisation (about 40 vector instructions for fp8, 48 for 4-bit) spread
     // evenly over this step's 2 MT MFMAs
     constexpr int VPM = ((WQ == WQ_F8 ? 40 : 48) + 2 * MT - 1) / (2 * MT);
@@ -609,10 +609,10 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);  // LDS reads of the next step's A fragments
 #pragma unroll
         for (int q = 0; q < 2 * MT; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            if (q < MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // an LDS read of the next step's A
             __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // then vector ALU work
         }
     };
