@@ -122,6 +122,11 @@ EDGE = [
     ("tiled_rows_fp8", C1.with_(T=2048, H=256, I=128, Is=128, expert="fp8", planted=0)),
     ("softmax_gated_fp8", C1.with_(T=300, H=256, I=128, Is=128, expert="fp8", route="softmax", shared_gate=True,
                                    planted=0)),
+    # one 64-wide k stage in both GEMMs (H = I = Is = 64) with tiles on: every tiled kernel's
+    # prologue and loop run a single stage
+    ("tiled_one_stage_bf16", C1.with_(T=400, H=64, E=8, K=2, G=1, TG=1, I=64, Is=64, planted=0)),
+    ("tiled_one_stage_q4", C1.with_(T=400, H=64, E=8, K=2, G=1, TG=1, I=64, Is=64, expert="q4", planted=0)),
+    ("tiled_one_stage_fp8", C1.with_(T=400, H=64, E=8, K=2, G=1, TG=1, I=64, Is=64, expert="fp8", planted=0)),
 ]
 
 
