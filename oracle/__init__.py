@@ -19,6 +19,7 @@ accuracy sweep of the fp32 exponential).  None is "parity unpinned".
 from __future__ import annotations
 
 import ctypes
+import hashlib
 import os
 import subprocess
 from typing import Optional, Sequence
@@ -32,14 +33,33 @@ DT_F32, DT_BF16, DT_Q4, DT_FP8 = 0, 1, 2, 3
 _DT = {"f32": DT_F32, "bf16": DT_BF16, "q4": DT_Q4, "fp8": DT_FP8}
 
 
+def _digest(cmd) -> str:
+    h = hashlib.sha256(" ".join(os.path.basename(c) for c in cmd).encode())
+    for f in ['oracle.c', 'oracle.h']:
+        with open(os.path.join(_HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def build(force: bool = False) -> str:
-    """Compile liboracle.so (gcc, OpenMP, no fast-math, no fp contraction)."""
-    if force or not os.path.exists(_SO):
-        cmd = ["gcc", "-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-mavx2", "-mfma", "-Wall", "-Wno-unknown-pragmas",
-               os.path.join(_HERE, "oracle.c"), "-o", _SO + ".tmp", "-lm"]
+    """Compile liboracle.so (gcc, OpenMP, no fast-math, no fp contraction).
+    Rebuilds when forced, when the library is missing, or when its sources or flags changed
+    since it was built (sha256 stamp beside it)."""
+    cmd = ["gcc", "-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-mavx2", "-mfma", "-Wall", "-Wno-unknown-pragmas",
+           os.path.join(_HERE, "oracle.c"), "-o", _SO + ".tmp", "-lm"]
+    stamp = _SO + ".sha256"
+    digest = _digest(cmd)
+    try:
+        with open(stamp) as fh:
+            current = os.path.exists(_SO) and fh.read().strip() == digest
+    except OSError:
+        current = False
+    if force or not current:
         subprocess.check_call(cmd)
         os.replace(_SO + ".tmp", _SO)
+        with open(stamp, "w") as fh:
+            fh.write(digest + "\n")
     return _SO
 
 
@@ -62,8 +82,12 @@ _lib = None
 def _L():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_SO)
+        # DSMOE_ORACLE_LIB: an alternative build of the same source (the sanitizer test builds one with
+        # AddressSanitizer / UndefinedBehaviorSanitizer and runs the pins against it)
+        path = os.environ.get("DSMOE_ORACLE_LIB")
+        if not path:
+            path = build()
+        lib = ctypes.CDLL(path)
         p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         lib.oracle_exp.restype = ctypes.c_float
         lib.oracle_exp.argtypes = [ctypes.c_float]
@@ -83,6 +107,8 @@ def _L():
         lib.oracle_forward.argtypes = [ctypes.POINTER(Layer), p, i64, p, p, p, p]
         lib.oracle_dense_mlp.restype = ctypes.c_int
         lib.oracle_dense_mlp.argtypes = [p, i32, i64, i32, i32, p, p, p, p]
+        lib.oracle_dispatch.restype = ctypes.c_int
+        lib.oracle_dispatch.argtypes = [p, i64, i32, i32, p, p, p, p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -243,12 +269,19 @@ def dispatch(inds: np.ndarray, E: int):
     """Expert-major grouping of the T*K token slots (slot s = t*K + j), the grouping that the
     gather_mm / gather_qmm expert calls imply ("Epic: Engine Inference Core Stage E - MoE +
     hybrid families", opening paragraph): experts ascending, slots ascending inside an expert.
-    Returns (counts [E], offsets [E+1], sorted_slot [T*K], slot_row [T*K]); a stable sort
-    (library primitive) is the definition."""
-    flat = np.asarray(inds).ravel().astype(np.int64)
-    counts = np.bincount(flat, minlength=E).astype(np.int32)
-    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    sorted_slot = np.argsort(flat, kind="stable").astype(np.int32)
-    slot_row = np.empty_like(sorted_slot)
-    slot_row[sorted_slot] = np.arange(len(flat), dtype=np.int32)
+    Returns (counts [E], offsets [E+1], sorted_slot [T*K], slot_row [T*K]) from the counting
+    sort ``oracle_dispatch`` in oracle.c; raises on an index outside [0, E)."""
+    inds = np.ascontiguousarray(inds, np.int32)
+    if inds.ndim != 2:
+        raise ValueError("inds must be [T, K]")
+    T, K = inds.shape
+    n = T * K
+    counts = np.full(E, -7, np.int32)
+    offsets = np.full(E + 1, -7, np.int32)
+    sorted_slot = np.full(n, -7, np.int32)
+    slot_row = np.full(n, -7, np.int32)
+    rc = _L().oracle_dispatch(_p(inds), T, max(K, 1), int(E), _p(counts), _p(offsets), _p(sorted_slot),
+                              _p(slot_row))
+    if rc != 0:
+        raise ValueError(f"oracle_dispatch rejected its arguments (rc={rc})")
     return counts, offsets, sorted_slot, slot_row

@@ -253,6 +253,13 @@ double oracle_e4m3(uint8_t c) {
     return sgn ? -v : v;
 }
 
+/* The 256 E4M3 values, each oracle_e4m3(c), filled once when the library loads, so that the
+ * expert loops look a code up instead of decoding it at every use (same values). */
+static double e4m3_value[256];
+__attribute__((constructor)) static void fill_e4m3_values(void) {
+    for (int c = 0; c < 256; ++c) e4m3_value[c] = oracle_e4m3((uint8_t)c);
+}
+
 /* element (o, i) of one expert matrix [out, in] in `dtype`:
  *   2 (q4): affine group-64 code, weight = s*q + b (s, b bf16 [out, in/64]);
  *   3 (fp8): E4M3 code times the fp32 scale of its 128 x 128 block (s fp32
@@ -269,7 +276,7 @@ static inline double w_at(const void* w, int32_t dtype, const void* s, const voi
     if (dtype == 3) {
         const int64_t nib = ((int64_t)in + 127) / 128;
         const double sc = (double)((const float*)s)[(o / 128) * nib + i / 128];
-        return oracle_e4m3(((const uint8_t*)w)[o * (int64_t)in + i]) * sc;
+        return e4m3_value[((const uint8_t*)w)[o * (int64_t)in + i]] * sc;
     }
     return (double)act_at(w, dtype, o * (int64_t)in + i);
 }
@@ -413,6 +420,41 @@ int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, d
     free(sc);
     free(o);
     free(sgl);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------
+ * dispatch
+ * ------------------------------------------------------------------------------------ */
+/*
+ * Expert dispatch ([Epic56] opening paragraph: forwardMoeWith hands each expert its tokens through
+ * gather_mm / gather_qmm).  The grouping written out as a counting sort, in three passes:
+ *   1. histogram: counts[e] = #{ s : inds[s] == e } over the slots s = t*K + j;
+ *   2. exclusive prefix sum: offsets[0] = 0, offsets[e+1] = offsets[e] + counts[e];
+ *   3. placement: walking the slots in ascending s, slot s goes to the next free row of its
+ *      expert's segment, so slots keep ascending order inside each expert (a stable sort);
+ *      slot_row records where each slot went.
+ */
+int oracle_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
+                    int32_t* sorted_slot, int32_t* slot_row) {
+    if (!counts || !offsets || T < 0 || K < 1 || E < 1) return -1;
+    const int64_t n = T * (int64_t)K;
+    if (n > 0 && (!inds || !sorted_slot || !slot_row)) return -1;
+    if (n >= ((int64_t)1 << 31)) return -1;
+    for (int64_t s = 0; s < n; ++s)
+        if (inds[s] < 0 || inds[s] >= E) return -1;
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t s = 0; s < n; ++s) counts[inds[s]] += 1;
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    for (int32_t e = 0; e < E; ++e) next[e] = offsets[e];
+    for (int64_t s = 0; s < n; ++s) {
+        const int32_t r = next[inds[s]]++;
+        sorted_slot[r] = (int32_t)s;
+        slot_row[s] = r;
+    }
+    free(next);
     return 0;
 }
 

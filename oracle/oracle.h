@@ -94,6 +94,14 @@ void oracle_swiglu(const double* x, int32_t H, int32_t I, int32_t dtype, const v
 int oracle_forward(const oracle_layer* L, const int64_t* rows, int64_t n_rows, double* y, int32_t* inds,
                    float* scores, float* logits);
 
+/* Dispatch: the expert-major grouping of the T*K token slots (slot s = t*K + j) behind the
+ * gather_mm / gather_qmm expert calls.  counts[e] = number of slots routed to e; offsets[e] =
+ * counts[0] + ... + counts[e-1], offsets[E] = T*K; sorted_slot[offsets[e] .. offsets[e+1]) are
+ * the slots routed to e in ascending order; slot_row[s] = the row r with sorted_slot[r] == s.
+ * Returns 0, or -1 on invalid arguments or an index outside [0, E) (outputs untouched). */
+int oracle_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
+                    int32_t* sorted_slot, int32_t* slot_row);
+
 /* Dense SwiGLU MLP over T rows of x ([T,H] act), weights [I,H], [I,H], [H,I] in act; y fp64 [T,H].
  * Returns 0, or -1 on invalid arguments. */
 int oracle_dense_mlp(const void* x, int32_t act, int64_t T, int32_t H, int32_t I, const void* wg, const void* wu,
