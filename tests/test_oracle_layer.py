@@ -220,3 +220,23 @@ def test_planted_rows_put_the_max_expert_in_a_losing_group():
     top = np.argmax(biased, axis=1)
     lost = [int(top[i]) not in set(inds[i].tolist()) for i in range(len(rows))]
     assert sum(lost) >= 32, sum(lost)
+
+
+@pytest.mark.parametrize("a,b_", [(2.5, 1.0), (0.75, 3.0)])
+def test_layer_scaling_linearity(a, b_):
+    """The routed part of y scales linearly with routed_scaling_factor (the gate page, "Algorithm":
+    the weights are multiplied by it after the norm): (y(a) - ys) = (a / b) (y(b) - ys), where ys
+    is the shared expert's output alone (the dense MLP of the shared weights), and the selection
+    does not depend on the factor.  Each weight is rounded once more in fp32 after the scaling, so
+    the two sides agree to a few fp32 ulps of the weights."""
+    w = synth.WORKLOADS["c1"].with_(T=24, H=128, I=64, Is=64, planted=0)
+    x, r, b, ex, sh = _inputs(w)
+    ya, ia, sa, _ = oracle.forward_workload(w.with_(rsf=a), x, r, b, ex, sh)
+    yb, ib, sb, _ = oracle.forward_workload(w.with_(rsf=b_), x, r, b, ex, sh)
+    assert np.array_equal(ia, ib)
+    ys = oracle.dense_mlp(x, sh["gate"], sh["up"], sh["down"], w.act)
+    ra, rb = ya - ys, (yb - ys) * (a / b_)
+    assert np.linalg.norm(ra) > 0.1 * np.linalg.norm(ya)  # the routed part is not negligible
+    assert np.linalg.norm(ra - rb) <= 4 * 2.0 ** -24 * np.linalg.norm(ra)
+    # and a wrong factor is visible at this tolerance
+    assert np.linalg.norm(ra - rb * 1.0001) > 4 * 2.0 ** -24 * np.linalg.norm(ra)
