@@ -21,6 +21,7 @@ contiguous; the router is ``[E, H]``; shared weights are ``[Is, H]``,
 from __future__ import annotations
 
 import ctypes
+import hashlib
 import math
 import os
 import subprocess
@@ -37,13 +38,32 @@ TID_X, TID_ROUTER, TID_BIAS, TID_WG, TID_WU, TID_WD = 1, 2, 3, 4, 5, 6
 TID_SWG, TID_SWU, TID_SWD, TID_ZIPF, TID_PLANT, TID_SGATE = 7, 8, 9, 10, 11, 12
 
 
+def _digest(cmd) -> str:
+    h = hashlib.sha256(" ".join(os.path.basename(c) for c in cmd).encode())
+    for f in ['synth.c']:
+        with open(os.path.join(_HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def build(force: bool = False) -> str:
-    """Compile libsynth.so with gcc (host code only)."""
-    if force or not os.path.exists(_SO):
-        cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
-               os.path.join(_HERE, "synth.c"), "-o", _SO + ".tmp", "-lm"]
+    """Compile libsynth.so with gcc (host code only).
+    Rebuilds when forced, when the library is missing, or when its sources or flags changed
+    since it was built (sha256 stamp beside it)."""
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+           os.path.join(_HERE, "synth.c"), "-o", _SO + ".tmp", "-lm"]
+    stamp = _SO + ".sha256"
+    digest = _digest(cmd)
+    try:
+        with open(stamp) as fh:
+            current = os.path.exists(_SO) and fh.read().strip() == digest
+    except OSError:
+        current = False
+    if force or not current:
         subprocess.check_call(cmd)
         os.replace(_SO + ".tmp", _SO)
+        with open(stamp, "w") as fh:
+            fh.write(digest + "\n")
     return _SO
 
 
@@ -53,8 +73,12 @@ _lib = None
 def _L():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_SO)
+        # DSMOE_SYNTH_LIB: an alternative build of the same source (the sanitizer test builds one with
+        # AddressSanitizer / UndefinedBehaviorSanitizer and runs the pins against it)
+        path = os.environ.get("DSMOE_SYNTH_LIB")
+        if not path:
+            path = build()
+        lib = ctypes.CDLL(path)
         u64, i64, d, p = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
         lib.synth_bits.restype = u64
         lib.synth_bits.argtypes = [u64, u64, u64]
