@@ -7,7 +7,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dsmoe_internal.hpp"
+#include "stage_hook.hpp"
 
 using namespace dsmoe;
 
@@ -143,13 +146,17 @@ int check_desc(const moe_layer_desc* d) {
 
 inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Per device: 0 unknown, 1 tiles of 256 rows fit in LDS, 2 only 128, 3 tiled kernels unusable.
-int g_tiled_state[64];
+// Per device: 1 tiles of 256 rows fit in LDS, 2 only 128, 3 tiled kernels unusable.  Found once
+// per device (the first call on it configures the tiled kernels' LDS limits); std::call_once
+// makes concurrent first calls safe.
+constexpr int MAX_DEVICES = 64;
+int g_tiled_state[MAX_DEVICES];
+std::once_flag g_tiled_once[MAX_DEVICES];
 
 int tiled_state() {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 3;
-    if (g_tiled_state[dev] == 0) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 3;
+    std::call_once(g_tiled_once[dev], [dev] {
         int lds = 0;
         hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
         int st = 3;
@@ -159,7 +166,7 @@ int tiled_state() {
         }
         (void)hipGetLastError();
         g_tiled_state[dev] = st;
-    }
+    });
     return g_tiled_state[dev];
 }
 
@@ -190,20 +197,17 @@ int check_dense(int64_t T, int32_t H, int32_t I, int32_t act) {
 }
 
 // measurement hook state (see moe_set_stage_events)
-struct StageHook {
-    int32_t stage = -1;
-    hipEvent_t const* events = nullptr;
-    int32_t n_pairs = 0;
-    int64_t calls = 0;
-};
-StageHook g_hook;
+StageHookRegistry g_hook;
 
-// records the hook's start (edge 0) or stop (edge 1) event of `stage` for the current call
-inline hipError_t mark(int32_t stage, int edge, hipStream_t s) {
-    if (g_hook.stage != stage || g_hook.n_pairs <= 0) return hipSuccess;
-    const int64_t i = g_hook.calls % g_hook.n_pairs;
-    return hipEventRecord(g_hook.events[2 * i + edge], s);
-}
+// the events one moe_forward call records (stage -1: none)
+struct HookCall {
+    HookPair p;
+    // records the start (edge 0) or stop (edge 1) event of `st` for this call
+    hipError_t mark(int32_t st, int edge, hipStream_t s) const {
+        if (st != p.stage) return hipSuccess;
+        return hipEventRecord((hipEvent_t)(edge ? p.stop : p.start), s);
+    }
+};
 
 }  // namespace
 
@@ -270,13 +274,7 @@ int moe_dense_mlp(int64_t T, int32_t H, int32_t I, int32_t act_dtype, const void
 }
 
 int moe_set_stage_events(int32_t stage, void* const* events, int32_t n_pairs) {
-    if (stage < -1 || stage > MOE_STAGE_COMBINE || n_pairs < 0 || (n_pairs > 0 && !events && stage >= 0))
-        return MOE_ERR_INVALID;
-    g_hook.stage = (stage < 0 || n_pairs == 0) ? -1 : stage;
-    g_hook.events = (hipEvent_t const*)events;
-    g_hook.n_pairs = g_hook.stage < 0 ? 0 : n_pairs;
-    g_hook.calls = 0;
-    return MOE_OK;
+    return g_hook.set(stage, events, n_pairs, MOE_STAGE_COMBINE) ? MOE_OK : MOE_ERR_INVALID;
 }
 
 const char* moe_strerror(int code) {
@@ -381,6 +379,8 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
     if (empty) return MOE_OK;
 
     hipStream_t s = (hipStream_t)stream;
+    const HookCall hook{g_hook.take()};
+    auto mark = [&hook](int32_t st, int edge, hipStream_t q) { return hook.mark(st, edge, q); };
     char* ws = (char*)workspace;
     float* logits = (float*)(ws + L.logits);
     float* sgl = (d->I_shared > 0 && sw->w_sgate) ? (float*)(ws + L.sgl) : nullptr;
@@ -492,7 +492,6 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
         return rc;
     if ((rc = hip_rc(launch_combine(a, d->act_dtype, scores, slot_row, sgl, y, s)))) return rc;
     if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 1, s)))) return rc;
-    ++g_hook.calls;
     return MOE_OK;
 }
 

@@ -24,7 +24,8 @@
  *   - Calls are asynchronous on `stream`: results are valid once the stream has synchronised.
  *     Nothing here synchronises the host or reads device memory back.
  *   - The library never allocates device memory: scratch comes from the caller's workspace.
- *     Concurrent calls need distinct workspaces.
+ *     Every entry point may be called from any host thread; calls that may run at the same time
+ *     on the device need distinct workspaces and outputs.
  *   - Results are bitwise deterministic from run to run (no atomics on floating-point data).
  *   - Layouts are row-major.  Stacked expert weights are [E, out, in] with `in` contiguous
  *     ([Epic56] "expert stacking" at load time).  bf16 tensors hold raw bf16 bit patterns.
@@ -259,9 +260,11 @@ int moe_dense_mlp(int64_t T, int32_t H, int32_t I, int32_t act_dtype, const void
  * into streaming and tiled kernels (see moe_forward), the GEMM1 and GEMM2 pairs bracket the
  * tiled launches only.  events are hipEvent_t handles
  * owned by the caller (created with timing enabled) and must outlive the hook.  stage = -1 (or
- * n_pairs = 0) clears the hook.  The hook is process-wide and not thread-safe: set it only
- * while one thread drives moe_forward.  Errors: -1 for a stage out of range, n_pairs < 0, or
- * NULL events with n_pairs > 0.
+ * n_pairs = 0) clears the hook.  The hook is process-wide: setting it and moe_forward calls may
+ * come from any thread (each call takes its event pair once, at entry, under a lock), but the
+ * calls of all threads advance one counter, so per-call timings are meaningful only while one
+ * thread drives moe_forward.  Errors: -1 for a stage out of range, n_pairs < 0, or NULL events
+ * with n_pairs > 0 (the hook is then unchanged).
  */
 #define MOE_STAGE_ROUTER 0
 #define MOE_STAGE_ROUTE 1
