@@ -226,17 +226,87 @@ def moe_forward_workspace_size(desc: LayerDesc) -> int:
     return int(load_library().moe_forward_workspace_size(ctypes.byref(desc)))
 
 
+_ACT_TORCH = {MOE_F32: "float32", MOE_BF16: "bfloat16"}
+
+
+def _shape_err(name, t, shape, dtypes) -> Optional[str]:
+    if t is None:
+        return f"{name} is missing"
+    if tuple(t.shape) != tuple(shape):
+        return f"{name} has shape {tuple(t.shape)}, the descriptor needs {tuple(shape)}"
+    if str(t.dtype).replace("torch.", "") not in dtypes:
+        return f"{name} has dtype {t.dtype}, the descriptor needs one of {dtypes}"
+    return None
+
+
+def forward_arg_errors(desc: LayerDesc, x, router_w, bias, experts: dict, shared: Optional[dict], y,
+                       logit_offset=None, inds_out=None, scores_out=None) -> list:
+    """Every mismatch between the tensors and the descriptor that moe_forward would hand to the
+    kernels (shape, dtype, contiguity), as messages; empty when they agree.  The kernels index
+    these buffers by the descriptor's sizes, so a mismatch here would read or write out of
+    bounds on the device."""
+    errs = []
+    T, H, E, I, Is, K = int(desc.T), int(desc.H), int(desc.E), int(desc.I), int(desc.I_shared), int(desc.route.top_k)
+    act = _ACT_TORCH.get(int(desc.act_dtype))
+    if act is None:
+        return [f"unsupported act_dtype {int(desc.act_dtype)}"]
+    wdt = int(desc.expert_dtype)
+    A = (act,)
+    for name, t, shape, dts in (("x", x, (T, H), A), ("y", y, (T, H), A), ("router_w", router_w, (E, H), A)):
+        errs.append(_shape_err(name, t, shape, dts))
+    if bias is not None or int(desc.route_kind) == MOE_ROUTE_DEEPSEEK:
+        errs.append(_shape_err("bias", bias, (E,), ("float32",)))
+    if logit_offset is not None:
+        errs.append(_shape_err("logit_offset", logit_offset, (E,), ("float32",)))
+    if inds_out is not None:
+        errs.append(_shape_err("inds_out", inds_out, (T, K), ("int32",)))
+    if scores_out is not None:
+        errs.append(_shape_err("scores_out", scores_out, (T, K), ("float32",)))
+    mats = (("gate", I, H), ("up", I, H), ("down", H, I))
+    for nm, o, i in mats:
+        t = experts.get(nm)
+        if wdt in (MOE_F32, MOE_BF16):
+            errs.append(_shape_err(f"experts[{nm!r}]", t, (E, o, i), (_ACT_TORCH[wdt],)))
+        elif wdt == MOE_Q4G64:
+            errs.append(_shape_err(f"experts[{nm!r}]", t, (E, o, i // 8), ("int32", "uint32")))
+            for side in ("s_", "b_"):
+                errs.append(_shape_err(f"experts[{side + nm!r}]", experts.get(side + nm), (E, o, i // 64),
+                                       ("bfloat16",)))
+        elif wdt == MOE_FP8:
+            errs.append(_shape_err(f"experts[{nm!r}]", t, (E, o, i), ("uint8",)))
+            errs.append(_shape_err(f"experts['s_{nm}']", experts.get("s_" + nm), (E, (o + 127) // 128, (i + 127) // 128),
+                                   ("float32",)))
+        else:
+            return [f"unsupported expert_dtype {wdt}"]
+    if Is > 0:
+        if shared is None:
+            errs.append("shared weights are missing (I_shared > 0)")
+        else:
+            for nm, shape in (("gate", (Is, H)), ("up", (Is, H)), ("down", (H, Is))):
+                errs.append(_shape_err(f"shared[{nm!r}]", shared.get(nm), shape, A))
+            if shared.get("sgate") is not None:
+                errs.append(_shape_err("shared['sgate']", shared.get("sgate"), (H,), A))
+    elif shared is not None:
+        errs.append("shared weights given but I_shared == 0")
+    errs = [e for e in errs if e]
+    tensors = [x, router_w, bias, y, logit_offset, inds_out, scores_out] + list(experts.values()) + \
+        ([] if shared is None else list(shared.values()))
+    if not _contig(*tensors):
+        errs.append("every tensor must be contiguous")
+    return errs
+
+
 def moe_forward(desc: LayerDesc, x, router_w, bias, experts: dict, shared: Optional[dict], y, logit_offset=None,
                 inds_out=None, scores_out=None, workspace=None, stream=None) -> int:
     """Whole MoE layer forward (see dsmoe.h).  experts: dict with 'gate', 'up', 'down' (and for
     4-bit weights 's_gate', 'b_gate', 's_up', 'b_up', 's_down', 'b_down'; for fp8 weights the
     fp32 block scales 's_gate', 's_up', 's_down'); shared: dict with
     'gate', 'up', 'down' (and optionally 'sgate', the [H] gate vector) or None.  bias may be
-    None with the softmax gate."""
-    import torch
-    if not _contig(x, router_w, bias, y, logit_offset, inds_out, scores_out, workspace):
+    None with the softmax gate.  Every tensor's shape and dtype is checked against the
+    descriptor first (forward_arg_errors); a mismatch returns MOE_ERR_INVALID with no launch."""
+    if forward_arg_errors(desc, x, router_w, bias, experts, shared, y, logit_offset, inds_out, scores_out):
         return MOE_ERR_INVALID
-    if bias is not None and (bias.dim() != 1 or bias.dtype != torch.float32):
+    if not _contig(workspace):
         return MOE_ERR_INVALID
     ew = ExpertWeights(*[_ptr(experts.get(k)) for k in
                          ("gate", "up", "down", "s_gate", "b_gate", "s_up", "b_up", "s_down", "b_down")])
