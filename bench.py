@@ -18,6 +18,7 @@ import ctypes
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -28,14 +29,39 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE-layer tokens/sec (DeepSeek-V3 shape, bf16) + % HBM/MFMA peak"
 
-# HBM-side traffic of the dominant kernel, GB per launch: rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE passes over this script, each scaled by what the same counter reads for the plain
-# 256 MiB device copy that main() runs first (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  The summaries
-# are kept with the kernel traces; an entry goes back to None whenever its kernel changes.
-TRAFFIC_GB = {
-    "c3": 12.86,  # gemm_dma<256, true>: 6,132,426 KiB fetched, 292,420 KiB written per launch
-    "c2": 7.47,  # stream_gemm<bf16, gate/up>: 3,645,204 KiB fetched, 2,305 KiB written per launch
+# Memory-side traffic of the dominant kernel, GB per launch, comes from a committed counter
+# summary under profiles/ (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, over this script, each
+# scaled by what the same counter reads for the plain 256 MiB device copy that main() runs
+# first).  FETCH_SIZE counts the L2's reads from the memory side, so it includes reads that the
+# memory-attached last-level cache serves.  The summary records the sha256 of the kernel's
+# source file when the counters were taken; if that file has changed since, the figure no longer
+# describes the kernel and "traffic" is null.
+TRAFFIC_PROFILES = {
+    "c3": ("gemm_dma_gate_up_dsv3_prefill_T8192_hbm_traffic.md", "experts_tiled.hip"),
+    "c2": ("stream_gemm_gate_up_dsv3_decode_T64_hbm_traffic.md", "experts.hip"),
 }
+
+
+def traffic_gb(workload: str):
+    """(GB per launch, summary file) from the committed summary, or (None, reason)."""
+    import hashlib
+    import re
+    if workload not in TRAFFIC_PROFILES:
+        return None, "no counter summary for this workload"
+    prof, src = TRAFFIC_PROFILES[workload]
+    path = os.path.join(ROOT, "profiles", prof)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None, f"profiles/{prof} missing"
+    m_gb = re.search(r"^traffic_gb_per_launch:\s*([0-9.]+)\s*$", text, re.M)
+    m_sha = re.search(r"^source_sha256:\s*(\S+)\s+(\S+)\s*$", text, re.M)
+    if not (m_gb and m_sha) or m_sha.group(1) != src:
+        return None, f"profiles/{prof} has no machine-readable figure"
+    cur = hashlib.sha256(open(os.path.join(ROOT, "deepseek_gate_expert_amd", "csrc", src), "rb").read()).hexdigest()
+    if cur != m_sha.group(2):
+        return None, f"{src} changed since the counters in profiles/{prof} were taken"
+    return float(m_gb.group(1)), f"profiles/{prof}"
 
 
 def log(msg):
@@ -159,27 +185,35 @@ def run_workload(name: str, steps: int, warmup: int, cache: dict):
     counts = np.bincount(inds.cpu().numpy().ravel(), minlength=w.E)
     n_hit = int(np.count_nonzero(counts))
 
-    ev = HipEvents(2 * steps + 2)
+    # events: pairs (2 i, 2 i + 1) around the dominant kernel of step i (the library records them),
+    # then steps + 1 step boundaries recorded here on the same stream
+    ev = HipEvents(2 * steps + steps + 1)
+    bnd = [2 * steps + i for i in range(steps + 1)]
     assert dg.moe_set_stage_events(dg.MOE_STAGE_GEMM1, ev.arr, steps) == 0
     try:
         torch.cuda.synchronize()
         hip = ev.hip
         hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-        hip.hipEventRecord(ev.arr[2 * steps], ctypes.c_void_p(stream.cuda_stream))
+        sp = ctypes.c_void_p(stream.cuda_stream)
         t0 = time.perf_counter()
-        for _ in range(steps):
+        hip.hipEventRecord(ev.arr[bnd[0]], sp)
+        for i in range(steps):
             step()
-        hip.hipEventRecord(ev.arr[2 * steps + 1], ctypes.c_void_p(stream.cuda_stream))
+            hip.hipEventRecord(ev.arr[bnd[i + 1]], sp)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        step_ms = ev.elapsed_ms(2 * steps, 2 * steps + 1) / steps
-        g1_ms = sum(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)) / steps
+        per_step = [ev.elapsed_ms(bnd[i], bnd[i + 1]) for i in range(steps)]
+        per_g1 = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
     finally:
         dg.moe_set_stage_events(-1, None, 0)
         ev.close()
-    log(f"[bench] {name}: {step_ms:.3f} ms/step (wall {wall_ms:.3f}), gemm1 {g1_ms:.3f} ms, experts hit {n_hit}, "
+    step_ms, g1_ms = statistics.median(per_step), statistics.median(per_g1)
+    mean_ms = sum(per_step) / steps
+    log(f"[bench] {name}: median {step_ms:.3f} ms/step (mean {mean_ms:.3f}, min {min(per_step):.3f}, "
+        f"max {max(per_step):.3f}; wall {wall_ms:.3f}), gemm1 median {g1_ms:.3f} ms, experts hit {n_hit}, "
         f"max load {counts.max()}")
-    return dict(w=w, step_ms=step_ms, wall_ms=wall_ms, gemm1_ms=g1_ms, n_hit=n_hit, max_load=int(counts.max()),
+    return dict(w=w, step_ms=step_ms, mean_ms=mean_ms, wall_ms=wall_ms, gemm1_ms=g1_ms, n_hit=n_hit,
+                max_load=int(counts.max()),
                 counts=counts,
                 x=x, bias=bias, offset=offset, router=router, experts=experts, shared=shared)
 
@@ -213,15 +247,16 @@ def run_dense(steps: int, warmup: int):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = HipEvents(2)
+    ev = HipEvents(steps + 1)
     stream = torch.cuda.current_stream()
     ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    ev.hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
-    for _ in range(steps):
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ev.hip.hipEventRecord(ev.arr[0], sp)
+    for i in range(steps):
         step()
-    ev.hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+        ev.hip.hipEventRecord(ev.arr[i + 1], sp)
     torch.cuda.synchronize()
-    ms = ev.elapsed_ms(0, 1) / steps
+    ms = statistics.median(ev.elapsed_ms(i, i + 1) for i in range(steps))
     ev.close()
     flops = 6.0 * T * H * I
     ach = flops / (ms / 1e3) / 1e12
@@ -311,10 +346,12 @@ def main():
         wl = res["w"]
         tps = wl.T / (res["step_ms"] / 1e3)
         decode = wl.T <= 256
+        tr, tr_src = traffic_gb(wl.name)
         if decode:
             ach = gemm1_bytes(wl, res["n_hit"]) / (res["gemm1_ms"] / 1e3) / 1e9
             roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                    "traffic": TRAFFIC_GB.get(wl.name), "traffic_unit": "GB per launch",
+                    "traffic": tr, "traffic_unit": "GB per launch (memory-side reads + writes)",
+                    "traffic_source": tr_src,
                     "kernel": f"stream_gemm<{wl.expert}, gate/up> (weight-streaming gate/up + SwiGLU)"}
             layer = layer_bytes(wl, res["n_hit"]) / (res["step_ms"] / 1e3) / 1e9
             roof["layer_achieved"] = layer
@@ -322,8 +359,8 @@ def main():
         else:
             ach = tiled_gemm1_flops(wl, res["counts"]) / (res["gemm1_ms"] / 1e3) / 1e12
             roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": ach / PEAK_BF16_TFLOPS, "traffic": TRAFFIC_GB.get(wl.name),
-                    "traffic_unit": "GB per launch",
+                    "frac": ach / PEAK_BF16_TFLOPS, "traffic": tr,
+                    "traffic_unit": "GB per launch (memory-side reads + writes)", "traffic_source": tr_src,
                     "kernel": ("gemm_dma<256, true> (tiled gate/up + SwiGLU: groups above 64 rows and the "
                                "shared expert)") if wl.expert == "bf16" else
                               (f"tiled gate/up + SwiGLU kernels: gemm_dma_wq<{wl.expert}, true> for the {wl.expert} "

@@ -61,6 +61,9 @@ class DeviceLayer:
     shared: Optional[dict]
     offset: Optional[torch.Tensor] = None
     workspace: Optional[torch.Tensor] = None
+    # test aid: before every call, fill the workspace and the fresh outputs with 0xFF bytes (NaN in
+    # bf16 and fp32, -1 in int32), so anything the kernels read without having written shows up
+    poison: bool = False
 
     def ensure_workspace(self):
         need = moe_forward_workspace_size(self.desc)
@@ -72,6 +75,8 @@ class DeviceLayer:
 
     def forward(self, x: torch.Tensor, y: torch.Tensor, inds=None, scores=None, stream=None) -> int:
         self.ensure_workspace()
+        if self.poison:
+            self.workspace.fill_(0xFF)
         return moe_forward(self.desc, x, self.router, self.bias, self.experts, self.shared, y, self.offset, inds,
                            scores, self.workspace, stream)
 
@@ -81,6 +86,10 @@ class DeviceLayer:
         K = self.desc.route.top_k
         inds = torch.empty((T, K), dtype=torch.int32, device=x.device) if want_route else None
         scores = torch.empty((T, K), dtype=torch.float32, device=x.device) if want_route else None
+        if self.poison:
+            for t in (y, inds, scores):
+                if t is not None:
+                    t.view(torch.uint8).fill_(0xFF)
         rc = self.forward(x, y, inds, scores)
         if rc != MOE_OK:
             raise RuntimeError(f"moe_forward failed: {rc} ({moe_strerror(rc)})")
@@ -96,7 +105,7 @@ def make_desc(w, T: Optional[int] = None) -> LayerDesc:
 
 def upload_layer(w, router: np.ndarray, bias: np.ndarray, experts: dict, shared: Optional[dict],
                  offset: Optional[np.ndarray], device, T: Optional[int] = None,
-                 shared_gate: Optional[np.ndarray] = None) -> DeviceLayer:
+                 shared_gate: Optional[np.ndarray] = None, poison: bool = False) -> DeviceLayer:
     dev = torch.device(device)
     ex = {k: to_device(v, dev) for k, v in experts.items()}
     sh = None if shared is None else {k: to_device(v, dev) for k, v in shared.items()}
@@ -104,4 +113,4 @@ def upload_layer(w, router: np.ndarray, bias: np.ndarray, experts: dict, shared:
         sh["sgate"] = to_device(shared_gate, dev)
     off = None if offset is None else to_device(np.ascontiguousarray(offset, np.float32), dev)
     return DeviceLayer(make_desc(w, T), to_device(router, dev), to_device(np.ascontiguousarray(bias, np.float32), dev),
-                       ex, sh, off)
+                       ex, sh, off, poison=poison)

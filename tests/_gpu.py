@@ -78,7 +78,7 @@ class Case:
         r_d, ex_d, sh_d = device_weights(w)
         from deepseek_gate_expert_amd.tensors import DeviceLayer, make_desc
         self.layer = DeviceLayer(make_desc(w), r_d, to_device(np.ascontiguousarray(self.bias, np.float32), DEV), ex_d,
-                                 sh_d, None if self.offset is None else to_device(self.offset, DEV))
+                                 sh_d, None if self.offset is None else to_device(self.offset, DEV), poison=True)
         self.x_d = to_device(self.x, DEV)
 
     def gpu(self):

@@ -31,10 +31,15 @@ def _case(T, H, I, act, seed=0):
 
 
 def _run(x, wg, wu, wd, act):
+    """The workspace and y are filled with 0xFF bytes (NaN) first, so an unwritten row shows up."""
     dt = torch.bfloat16 if act == "bf16" else torch.float32
     xd, g, u, d = (to_device(a, DEV) for a in (x, wg, wu, wd))
-    y = torch.empty((x.shape[0], x.shape[1]), dtype=dt, device=DEV)
-    rc = dg.moe_dense_mlp(xd, g, u, d, y)
+    T, H = x.shape
+    y = torch.empty((T, H), dtype=dt, device=DEV)
+    y.view(torch.uint8).fill_(0xFF)
+    ws = torch.full((max(1, dg.moe_dense_workspace_size(T, H, wg.shape[0], dg.act_code(dt))),), 0xFF,
+                    dtype=torch.uint8, device=DEV)
+    rc = dg.moe_dense_mlp(xd, g, u, d, y, ws)
     torch.cuda.synchronize()
     return rc, y
 
