@@ -209,6 +209,158 @@ struct HookCall {
     }
 };
 
+// Argument checks of moe_forward, all on the host, except those of the workspace.
+int check_forward(const moe_layer_desc* d, const void* x, const void* router_w, const float* bias,
+                  const float* logit_offset, const moe_expert_weights* ew, const moe_shared_weights* sw, const void* y,
+                  const int32_t* inds_out, const float* scores_out) {
+    int rc = check_desc(d);
+    if (rc != MOE_OK) return rc;
+    const bool empty = d->T == 0;
+    const bool softmax = d->route_kind == MOE_ROUTE_SOFTMAX;
+    if (!ptr_ok(x, empty) || !ptr_ok(router_w, false) || !ptr_ok(bias, softmax) || !ptr_ok(logit_offset, true) ||
+        !ptr_ok(y, empty) || !ptr_ok(inds_out, true) || !ptr_ok(scores_out, true))
+        return MOE_ERR_INVALID;
+    if (!ew || !ptr_ok(ew->w_gate, false) || !ptr_ok(ew->w_up, false) || !ptr_ok(ew->w_down, false))
+        return MOE_ERR_INVALID;
+    if (d->expert_dtype == MOE_Q4G64 &&
+        (!ptr_ok(ew->s_gate, false) || !ptr_ok(ew->b_gate, false) || !ptr_ok(ew->s_up, false) ||
+         !ptr_ok(ew->b_up, false) || !ptr_ok(ew->s_down, false) || !ptr_ok(ew->b_down, false)))
+        return MOE_ERR_INVALID;
+    if (d->expert_dtype == MOE_FP8 &&
+        (!ptr_ok(ew->s_gate, false) || !ptr_ok(ew->s_up, false) || !ptr_ok(ew->s_down, false)))
+        return MOE_ERR_INVALID;
+    if (d->I_shared > 0) {
+        if (!sw || !ptr_ok(sw->w_gate, false) || !ptr_ok(sw->w_up, false) || !ptr_ok(sw->w_down, false) ||
+            !ptr_ok(sw->w_sgate, true))
+            return MOE_ERR_INVALID;
+    } else if (sw) {
+        return MOE_ERR_INVALID;
+    }
+    return MOE_OK;
+}
+
+// The launch sequence of the layer into a checked workspace `ws` laid out as L (T > 0).
+int launch_forward(const moe_layer_desc* d, const void* x, const void* router_w, const float* bias,
+                   const float* logit_offset, const moe_expert_weights* ew, const moe_shared_weights* sw, void* y,
+                   int32_t* inds_out, float* scores_out, char* ws, const FwdLayout& L, void* stream) {
+    int rc = MOE_OK;
+    const bool softmax = d->route_kind == MOE_ROUTE_SOFTMAX;
+    hipStream_t s = (hipStream_t)stream;
+    const HookCall hook{g_hook.take()};
+    auto mark = [&hook](int32_t st, int edge, hipStream_t q) { return hook.mark(st, edge, q); };
+    float* logits = (float*)(ws + L.logits);
+    float* sgl = (d->I_shared > 0 && sw->w_sgate) ? (float*)(ws + L.sgl) : nullptr;
+    int32_t* inds = inds_out ? inds_out : (int32_t*)(ws + L.inds);
+    float* scores = scores_out ? scores_out : (float*)(ws + L.scores);
+    int32_t* blk = (int32_t*)(ws + L.blk);
+    int32_t* counts = (int32_t*)(ws + L.counts);
+    int32_t* offsets = (int32_t*)(ws + L.offsets);
+    int32_t* sorted_slot = (int32_t*)(ws + L.sorted_slot);
+    int32_t* slot_row = (int32_t*)(ws + L.slot_row);
+    int32_t* tile_count = (int32_t*)(ws + L.tiles);
+    int32_t* tile_info = tile_count + 64;  // keep the entries 256-byte aligned
+
+    if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 0, s)))) return rc;
+    if ((rc = hip_rc(launch_router(x, router_w, d->act_dtype, d->T, d->H, d->E, logit_offset, logits, s))))
+        return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 1, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_ROUTE, 0, s)))) return rc;
+    if ((rc = hip_rc(softmax ? launch_route_softmax(logits, d->T, d->E, d->route.top_k, inds, scores, s)
+                             : launch_route(logits, d->T, d->E, bias, d->route, inds, scores, s))))
+        return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_ROUTE, 1, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_DISPATCH, 0, s)))) return rc;
+    if ((rc = hip_rc(launch_dispatch(inds, d->T, d->route.top_k, d->E, counts, offsets, sorted_slot, slot_row, blk,
+                                     s))))
+        return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_DISPATCH, 1, s)))) return rc;
+
+    GroupedArgs a;
+    memset(&a, 0, sizeof(a));
+    a.T = d->T;
+    a.H = d->H;
+    a.E = d->E;
+    a.I = d->I;
+    a.Is = d->I_shared;
+    a.K = d->route.top_k;
+    a.TK = (int32_t)(d->T * d->route.top_k);
+    a.ldh = d->I > d->I_shared ? d->I : d->I_shared;
+    a.offsets = offsets;
+    a.sorted_slot = sorted_slot;
+    a.inds = inds;
+    a.x = x;
+    a.h = ws + L.h;
+    a.o = ws + L.o;
+    a.wg = ew->w_gate;
+    a.wu = ew->w_up;
+    a.wd = ew->w_down;
+    if (d->expert_dtype == MOE_Q4G64) {
+        a.sg = (const bf16_t*)ew->s_gate;
+        a.bg = (const bf16_t*)ew->b_gate;
+        a.su = (const bf16_t*)ew->s_up;
+        a.bu = (const bf16_t*)ew->b_up;
+        a.sd = (const bf16_t*)ew->s_down;
+        a.bd = (const bf16_t*)ew->b_down;
+    } else if (d->expert_dtype == MOE_FP8) {
+        a.fsg = (const float*)ew->s_gate;
+        a.fsu = (const float*)ew->s_up;
+        a.fsd = (const float*)ew->s_down;
+    }
+    if (d->I_shared > 0) {
+        a.swg = sw->w_gate;
+        a.swu = sw->w_up;
+        a.swd = sw->w_down;
+    }
+
+    const int32_t E = d->E;
+    const int32_t gend = E + (d->I_shared > 0 ? 1 : 0);
+    const bool f32 = d->act_dtype == MOE_F32;
+    const bool quant = d->expert_dtype == MOE_Q4G64 || d->expert_dtype == MOE_FP8;
+    TilePlan tp{false, 128, 128, 0, STREAM_MAX_ROWS};
+    if (!f32) {
+        const int ts = tiled_state();
+        if (ts != 3) tp = plan_tiles(d, ts == 1);
+    }
+    a.stream_max_rows = tp.on ? tp.min_rows : 0x7fffffff;
+    const int32_t rdt = quant ? d->expert_dtype : MOE_BF16;
+    const int32_t split = quant ? E : gend;  // tiled: quantised routed groups vs the bf16 (shared) group
+    // weight-streaming kernels of one expert-GEMM pass (groups of at most stream_max_rows rows);
+    // one launch covers the routed groups and the shared expert, which streams its bf16 weights
+    // also in quantised layers
+    auto streamed = [&](bool first) -> int {
+        if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));
+        if (tp.on && tp.min_rows == 0) return MOE_OK;  // every group is tiled
+        return hip_rc(first ? launch_gemm1_bf16(a, 0, gend, rdt, s) : launch_gemm2_bf16(a, 0, gend, rdt, s));
+    };
+    // tiled kernels of one pass (the other groups)
+    auto tiled = [&](bool first) -> int {
+        if (!tp.on) return MOE_OK;
+        int r = hip_rc(launch_gemm_tiled(a, first, tp.BM, 0, split, rdt, tile_count, tile_info, tp.max_tiles, s));
+        if (!r && split < gend)
+            r = hip_rc(launch_gemm_tiled(a, first, tp.BMs, split, gend, MOE_BF16, tile_count, tile_info,
+                                         tp.max_tiles, s));
+        return r;
+    };
+    if (tp.on && (rc = hip_rc(launch_tiles(a, tp.BM, tp.BMs, tp.min_rows, tile_count, tile_info, s)))) return rc;
+    // With tiles on, the GEMM1 / GEMM2 stage events bracket the tiled kernels only (the
+    // dominant kernels of prefill layers); the streaming kernels run right before them.
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool first = pass == 0;
+        const int32_t stage = first ? MOE_STAGE_GEMM1 : MOE_STAGE_GEMM2;
+        if (!tp.on && (rc = hip_rc(mark(stage, 0, s)))) return rc;
+        if ((rc = streamed(first))) return rc;
+        if (tp.on && (rc = hip_rc(mark(stage, 0, s)))) return rc;
+        if ((rc = tiled(first))) return rc;
+        if ((rc = hip_rc(mark(stage, 1, s)))) return rc;
+    }
+    if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 0, s)))) return rc;
+    if (sgl && (rc = hip_rc(launch_router(x, sw->w_sgate, d->act_dtype, d->T, d->H, 1, nullptr, sgl, s))))
+        return rc;
+    if ((rc = hip_rc(launch_combine(a, d->act_dtype, scores, slot_row, sgl, y, s)))) return rc;
+    if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 1, s)))) return rc;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,149 +502,14 @@ size_t moe_forward_workspace_size(const moe_layer_desc* d) {
 int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, const float* bias,
                 const float* logit_offset, const moe_expert_weights* ew, const moe_shared_weights* sw, void* y,
                 int32_t* inds_out, float* scores_out, void* workspace, size_t workspace_bytes, void* stream) {
-    int rc = check_desc(d);
+    const int rc = check_forward(d, x, router_w, bias, logit_offset, ew, sw, y, inds_out, scores_out);
     if (rc != MOE_OK) return rc;
-    const bool empty = d->T == 0;
-    const bool softmax = d->route_kind == MOE_ROUTE_SOFTMAX;
-    if (!ptr_ok(x, empty) || !ptr_ok(router_w, false) || !ptr_ok(bias, softmax) || !ptr_ok(logit_offset, true) ||
-        !ptr_ok(y, empty) || !ptr_ok(inds_out, true) || !ptr_ok(scores_out, true))
-        return MOE_ERR_INVALID;
-    if (!ew || !ptr_ok(ew->w_gate, false) || !ptr_ok(ew->w_up, false) || !ptr_ok(ew->w_down, false))
-        return MOE_ERR_INVALID;
-    if (d->expert_dtype == MOE_Q4G64 &&
-        (!ptr_ok(ew->s_gate, false) || !ptr_ok(ew->b_gate, false) || !ptr_ok(ew->s_up, false) ||
-         !ptr_ok(ew->b_up, false) || !ptr_ok(ew->s_down, false) || !ptr_ok(ew->b_down, false)))
-        return MOE_ERR_INVALID;
-    if (d->expert_dtype == MOE_FP8 &&
-        (!ptr_ok(ew->s_gate, false) || !ptr_ok(ew->s_up, false) || !ptr_ok(ew->s_down, false)))
-        return MOE_ERR_INVALID;
-    if (d->I_shared > 0) {
-        if (!sw || !ptr_ok(sw->w_gate, false) || !ptr_ok(sw->w_up, false) || !ptr_ok(sw->w_down, false) ||
-            !ptr_ok(sw->w_sgate, true))
-            return MOE_ERR_INVALID;
-    } else if (sw) {
-        return MOE_ERR_INVALID;
-    }
     const FwdLayout L = fwd_layout(d);
     if (!ptr_ok(workspace, false) || ((uintptr_t)workspace & (ALIGN - 1))) return MOE_ERR_INVALID;
     if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
-    if (empty) return MOE_OK;
-
-    hipStream_t s = (hipStream_t)stream;
-    const HookCall hook{g_hook.take()};
-    auto mark = [&hook](int32_t st, int edge, hipStream_t q) { return hook.mark(st, edge, q); };
-    char* ws = (char*)workspace;
-    float* logits = (float*)(ws + L.logits);
-    float* sgl = (d->I_shared > 0 && sw->w_sgate) ? (float*)(ws + L.sgl) : nullptr;
-    int32_t* inds = inds_out ? inds_out : (int32_t*)(ws + L.inds);
-    float* scores = scores_out ? scores_out : (float*)(ws + L.scores);
-    int32_t* blk = (int32_t*)(ws + L.blk);
-    int32_t* counts = (int32_t*)(ws + L.counts);
-    int32_t* offsets = (int32_t*)(ws + L.offsets);
-    int32_t* sorted_slot = (int32_t*)(ws + L.sorted_slot);
-    int32_t* slot_row = (int32_t*)(ws + L.slot_row);
-    int32_t* tile_count = (int32_t*)(ws + L.tiles);
-    int32_t* tile_info = tile_count + 64;  // keep the entries 256-byte aligned
-
-    if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 0, s)))) return rc;
-    if ((rc = hip_rc(launch_router(x, router_w, d->act_dtype, d->T, d->H, d->E, logit_offset, logits, s))))
-        return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_ROUTER, 1, s)))) return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_ROUTE, 0, s)))) return rc;
-    if ((rc = hip_rc(softmax ? launch_route_softmax(logits, d->T, d->E, d->route.top_k, inds, scores, s)
-                             : launch_route(logits, d->T, d->E, bias, d->route, inds, scores, s))))
-        return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_ROUTE, 1, s)))) return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_DISPATCH, 0, s)))) return rc;
-    if ((rc = hip_rc(launch_dispatch(inds, d->T, d->route.top_k, d->E, counts, offsets, sorted_slot, slot_row, blk,
-                                     s))))
-        return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_DISPATCH, 1, s)))) return rc;
-
-    GroupedArgs a;
-    memset(&a, 0, sizeof(a));
-    a.T = d->T;
-    a.H = d->H;
-    a.E = d->E;
-    a.I = d->I;
-    a.Is = d->I_shared;
-    a.K = d->route.top_k;
-    a.TK = (int32_t)(d->T * d->route.top_k);
-    a.ldh = d->I > d->I_shared ? d->I : d->I_shared;
-    a.offsets = offsets;
-    a.sorted_slot = sorted_slot;
-    a.inds = inds;
-    a.x = x;
-    a.h = ws + L.h;
-    a.o = ws + L.o;
-    a.wg = ew->w_gate;
-    a.wu = ew->w_up;
-    a.wd = ew->w_down;
-    if (d->expert_dtype == MOE_Q4G64) {
-        a.sg = (const bf16_t*)ew->s_gate;
-        a.bg = (const bf16_t*)ew->b_gate;
-        a.su = (const bf16_t*)ew->s_up;
-        a.bu = (const bf16_t*)ew->b_up;
-        a.sd = (const bf16_t*)ew->s_down;
-        a.bd = (const bf16_t*)ew->b_down;
-    } else if (d->expert_dtype == MOE_FP8) {
-        a.fsg = (const float*)ew->s_gate;
-        a.fsu = (const float*)ew->s_up;
-        a.fsd = (const float*)ew->s_down;
-    }
-    if (d->I_shared > 0) {
-        a.swg = sw->w_gate;
-        a.swu = sw->w_up;
-        a.swd = sw->w_down;
-    }
-
-    const int32_t E = d->E;
-    const int32_t gend = E + (d->I_shared > 0 ? 1 : 0);
-    const bool f32 = d->act_dtype == MOE_F32;
-    const bool quant = d->expert_dtype == MOE_Q4G64 || d->expert_dtype == MOE_FP8;
-    TilePlan tp{false, 128, 128, 0, STREAM_MAX_ROWS};
-    if (!f32) {
-        const int ts = tiled_state();
-        if (ts != 3) tp = plan_tiles(d, ts == 1);
-    }
-    a.stream_max_rows = tp.on ? tp.min_rows : 0x7fffffff;
-    const int32_t rdt = quant ? d->expert_dtype : MOE_BF16;
-    const int32_t split = quant ? E : gend;  // tiled: quantised routed groups vs the bf16 (shared) group
-    // weight-streaming kernels of one expert-GEMM pass (groups of at most stream_max_rows rows);
-    // one launch covers the routed groups and the shared expert, which streams its bf16 weights
-    // also in quantised layers
-    auto streamed = [&](bool first) -> int {
-        if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));
-        if (tp.on && tp.min_rows == 0) return MOE_OK;  // every group is tiled
-        return hip_rc(first ? launch_gemm1_bf16(a, 0, gend, rdt, s) : launch_gemm2_bf16(a, 0, gend, rdt, s));
-    };
-    // tiled kernels of one pass (the other groups)
-    auto tiled = [&](bool first) -> int {
-        if (!tp.on) return MOE_OK;
-        int r = hip_rc(launch_gemm_tiled(a, first, tp.BM, 0, split, rdt, tile_count, tile_info, tp.max_tiles, s));
-        if (!r && split < gend)
-            r = hip_rc(launch_gemm_tiled(a, first, tp.BMs, split, gend, MOE_BF16, tile_count, tile_info,
-                                         tp.max_tiles, s));
-        return r;
-    };
-    if (tp.on && (rc = hip_rc(launch_tiles(a, tp.BM, tp.BMs, tp.min_rows, tile_count, tile_info, s)))) return rc;
-    // With tiles on, the GEMM1 / GEMM2 stage events bracket the tiled kernels only (the
-    // dominant kernels of prefill layers); the streaming kernels run right before them.
-    for (int pass = 0; pass < 2; ++pass) {
-        const bool first = pass == 0;
-        const int32_t stage = first ? MOE_STAGE_GEMM1 : MOE_STAGE_GEMM2;
-        if (!tp.on && (rc = hip_rc(mark(stage, 0, s)))) return rc;
-        if ((rc = streamed(first))) return rc;
-        if (tp.on && (rc = hip_rc(mark(stage, 0, s)))) return rc;
-        if ((rc = tiled(first))) return rc;
-        if ((rc = hip_rc(mark(stage, 1, s)))) return rc;
-    }
-    if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 0, s)))) return rc;
-    if (sgl && (rc = hip_rc(launch_router(x, sw->w_sgate, d->act_dtype, d->T, d->H, 1, nullptr, sgl, s))))
-        return rc;
-    if ((rc = hip_rc(launch_combine(a, d->act_dtype, scores, slot_row, sgl, y, s)))) return rc;
-    if ((rc = hip_rc(mark(MOE_STAGE_COMBINE, 1, s)))) return rc;
-    return MOE_OK;
+    if (d->T == 0) return MOE_OK;
+    return launch_forward(d, x, router_w, bias, logit_offset, ew, sw, y, inds_out, scores_out, (char*)workspace, L,
+                          stream);
 }
 
 }  // extern "C"
