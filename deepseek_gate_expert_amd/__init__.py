@@ -28,7 +28,8 @@ MOE_ROUTE_DEEPSEEK, MOE_ROUTE_SOFTMAX = 0, 1
 MOE_STAGE_ROUTER, MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE = range(6)
 EXPORTS = ("moe_router_logits", "moe_route_deepseek", "moe_route_softmax", "moe_dispatch_workspace_size", "moe_dispatch",
            "moe_forward_workspace_size", "moe_forward", "moe_dense_workspace_size", "moe_dense_mlp",
-           "moe_set_stage_events", "moe_strerror")
+           "moe_set_stage_events", "moe_strerror", "moe_forward_static")
+MOE_STATIC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 class RouteParams(ctypes.Structure):
@@ -88,6 +89,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.moe_forward.restype = ctypes.c_int
         lib.moe_forward.argtypes = [ctypes.POINTER(LayerDesc), p, p, p, p, ctypes.POINTER(ExpertWeights),
                                     ctypes.POINTER(SharedWeights), p, p, p, p, sz, p]
+        lib.moe_forward_static.restype = ctypes.c_int
+        lib.moe_forward_static.argtypes = [ctypes.POINTER(LayerDesc), p, p, p, p, ctypes.POINTER(ExpertWeights),
+                                           ctypes.POINTER(SharedWeights), p, p, p, p]
         lib.moe_set_stage_events.restype = ctypes.c_int
         lib.moe_set_stage_events.argtypes = [i32, p, i32]
         _lib = lib
@@ -321,6 +325,28 @@ def moe_forward(desc: LayerDesc, x, router_w, bias, experts: dict, shared: Optio
     return load_library().moe_forward(ctypes.byref(desc), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(logit_offset),
                                       ctypes.byref(ew), None if sw is None else ctypes.byref(sw), _ptr(y),
                                       _ptr(inds_out), _ptr(scores_out), _ptr(workspace), nbytes, _stream(stream))
+
+
+def moe_forward_static(desc: LayerDesc, x, router_w, bias, experts: dict, shared: Optional[dict], y,
+                       logit_offset=None, inds_out=None, scores_out=None, stream=None) -> int:
+    """moe_forward with the library's own fixed scratch instead of a workspace (see dsmoe.h):
+    for callers that cannot allocate; MOE_ERR_WORKSPACE when the layer needs more scratch than
+    MOE_STATIC_SCRATCH_BYTES.  Same argument checks as moe_forward."""
+    if forward_arg_errors(desc, x, router_w, bias, experts, shared, y, logit_offset, inds_out, scores_out):
+        return MOE_ERR_INVALID
+    ew = ExpertWeights(*[_ptr(experts.get(k)) for k in
+                         ("gate", "up", "down", "s_gate", "b_gate", "s_up", "b_up", "s_down", "b_down")])
+    sw = None
+    if shared is not None:
+        sw = SharedWeights(_ptr(shared["gate"]), _ptr(shared["up"]), _ptr(shared["down"]), _ptr(shared.get("sgate")))
+    tensors = [x, router_w, bias, y, logit_offset, inds_out, scores_out] + \
+        [v for v in experts.values()] + ([] if shared is None else list(shared.values()))
+    if not _same_device(*tensors):
+        return MOE_ERR_INVALID
+    return load_library().moe_forward_static(ctypes.byref(desc), _ptr(x), _ptr(router_w), _ptr(bias),
+                                             _ptr(logit_offset), ctypes.byref(ew),
+                                             None if sw is None else ctypes.byref(sw), _ptr(y), _ptr(inds_out),
+                                             _ptr(scores_out), _stream(stream))
 
 
 def moe_dense_workspace_size(T: int, H: int, I: int, act_dtype: int) -> int:

@@ -361,6 +361,32 @@ int launch_forward(const moe_layer_desc* d, const void* x, const void* router_w,
     return MOE_OK;
 }
 
+// Scratch of moe_forward_static: one array per device, allocated by the runtime when the library's
+// code object is loaded on that device and held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device memory: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that address
+// is ever passed to kernels.
+__device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+void* g_scratch_ptr[MAX_DEVICES];
+hipError_t g_scratch_err[MAX_DEVICES];
+std::once_flag g_scratch_once[MAX_DEVICES];
+
+// device address of the current device's scratch array (MOE_ERR_HIP if it cannot be had)
+int static_scratch(void** ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MOE_ERR_HIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+        (void)hipGetLastError();
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return MOE_ERR_HIP;
+    *ptr = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -492,6 +518,19 @@ int moe_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E, int32_t* 
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
     return hip_rc(launch_dispatch(inds, T, K, E, counts, offsets, sorted_slot, slot_row, (int32_t*)workspace,
                                   (hipStream_t)stream));
+}
+
+int moe_forward_static(const moe_layer_desc* d, const void* x, const void* router_w, const float* bias,
+                       const float* logit_offset, const moe_expert_weights* ew, const moe_shared_weights* sw, void* y,
+                       int32_t* inds_out, float* scores_out, void* stream) {
+    int rc = check_forward(d, x, router_w, bias, logit_offset, ew, sw, y, inds_out, scores_out);
+    if (rc != MOE_OK) return rc;
+    const FwdLayout L = fwd_layout(d);
+    if (L.total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    if (d->T == 0) return MOE_OK;
+    void* ws = nullptr;
+    if ((rc = static_scratch(&ws)) != MOE_OK) return rc;
+    return launch_forward(d, x, router_w, bias, logit_offset, ew, sw, y, inds_out, scores_out, (char*)ws, L, stream);
 }
 
 size_t moe_forward_workspace_size(const moe_layer_desc* d) {

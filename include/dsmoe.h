@@ -232,6 +232,24 @@ int moe_forward(const moe_layer_desc* d, const void* x, const void* router_w, co
                 int32_t* inds_out, float* scores_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_forward without a workspace argument, for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  The
+ * layer, its arguments (other than the workspace), its results and its errors are those of
+ * moe_forward; the scratch is a fixed array of MOE_STATIC_SCRATCH_BYTES inside the library, one
+ * per device, allocated when the library's code is loaded on that device and held until the
+ * process ends.  The call allocates and frees nothing.  Layers whose
+ * moe_forward_workspace_size exceeds MOE_STATIC_SCRATCH_BYTES (at DeepSeek-V3 shapes, batches
+ * above 401 tokens) return MOE_ERR_WORKSPACE (-3) with no output written.
+ * Every call on a device uses that device's one array: calls whose kernels may overlap on the
+ * device (several streams, several threads) race on it and give undefined results; calls on one
+ * stream are safe.  Nothing in the array needs to start at zero.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
+int moe_forward_static(const moe_layer_desc* d, const void* x, const void* router_w, const float* bias,
+                       const float* logit_offset, const moe_expert_weights* ew, const moe_shared_weights* sw, void* y,
+                       int32_t* inds_out, float* scores_out, void* stream);
+
+/*
  * Dense SwiGLU MLP layer: y = W_down (silu(W_gate x) * (W_up x)) per token -- the dense layers
  * that DeepSeek models interleave with MoE layers ([Epic56] "Decision 5 superseded" item 2:
  * dense/MoE layer mixing); the computation is the shared expert's path on its own, with the same

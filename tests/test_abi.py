@@ -272,3 +272,21 @@ def test_dense_rejects(lib):
     assert f(16, 128, 64, 1, P, P, P, P, P, P, need - 1, None) == dg.MOE_ERR_WORKSPACE
     assert f(16, 96, 64, 1, P, P, P, P, P, P, need, None) == dg.MOE_ERR_UNSUPPORTED
     assert f(0, 128, 64, 1, None, P, P, P, None, P, need, None) == dg.MOE_OK
+
+
+def test_forward_static_host_checks(lib):
+    """moe_forward_static checks its arguments like moe_forward, then the scratch limit, all before
+    any HIP call: an invalid descriptor is -1, a layer needing more than the fixed scratch is -3,
+    and zero tokens is a no-op."""
+    def static(d, x=P, y=P, shared=True):
+        ew = dg.ExpertWeights(P, P, P)
+        sw = dg.SharedWeights(P, P, P) if shared else None
+        return lib.moe_forward_static(ctypes.byref(d), x, P, P, None, ctypes.byref(ew),
+                                      None if sw is None else ctypes.byref(sw), y, None, None, None)
+    assert static(desc(top_k=0)) == dg.MOE_ERR_INVALID
+    assert static(desc(), x=None) == dg.MOE_ERR_INVALID
+    assert static(desc(), shared=False) == dg.MOE_ERR_INVALID
+    big = dg.layer_desc(8192, 7168, 256, 2048, 2048, 1, 1, 8, 8, 4, True, 2.5)
+    assert lib.moe_forward_workspace_size(ctypes.byref(big)) > dg.MOE_STATIC_SCRATCH_BYTES
+    assert static(big) == dg.MOE_ERR_WORKSPACE
+    assert static(desc(T=0), x=None, y=None) == dg.MOE_OK
