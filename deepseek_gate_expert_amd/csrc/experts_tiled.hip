@@ -428,6 +428,19 @@ struct Fmt {
 constexpr int ring_bytes(int wqt) {
     return wqt == WQ_F8 ? Fmt<WQ_F8>::NS * Fmt<WQ_F8>::STAGE : Fmt<WQ_Q4>::NS * Fmt<WQ_Q4>::STAGE;
 }
+// 4-bit tiles with the scales and offsets in chunks of 8 stages: a ring without side data plus two
+// chunk slots of [2 kinds][256 rows][16 bytes]
+constexpr int SIDE8_BYTES = 2 * 2 * 256 * 16;
+constexpr int ring_bytes_side8() {
+    return Fmt<WQ_Q4>::NS * (Fmt<WQ_Q4>::A_BYTES + Fmt<WQ_Q4>::C_BYTES) + SIDE8_BYTES;
+}
+// dynamic LDS of a launch: the stage ring, or the epilogue's bf16 image of the output tile
+// (bm x 128 for GEMM-1, bm x 256 for GEMM-2) when that is larger
+constexpr int lds_bytes(int wqt, bool swiglu, bool side8 = false) {
+    const int img = bm(wqt) * (swiglu ? 128 : 256) * 2;
+    const int ring = side8 ? ring_bytes_side8() : ring_bytes(wqt);
+    return ring > img ? ring : img;
+}
 template <int WQ>
 __device__ __forceinline__ int cswz(int rho) { return WQ == WQ_F8 ? (rho >> 1) & 3 : (rho >> 2) & 1; }
 }  // namespace wq
@@ -454,15 +467,18 @@ struct BStage<WQ_F8> {
 // Only those rows are staged and multiplied; the weights' codes and scales are staged and
 // dequantised once per tile whatever its height, so a group of up to 256 rows pays for its
 // dequantisation once.
-template <int WQ, bool SWIGLU, int MT>
+template <int WQ, bool SWIGLU, bool SIDE8, int MT>
 __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t g, int32_t m0, int32_t r0,
                                         int32_t cnt, int32_t n0) {
     using namespace dma;
     using F = wq::Fmt<WQ>;
+    static_assert(!SIDE8 || WQ == WQ_Q4, "chunked side data is a 4-bit layout");
     constexpr int NS = F::NS;
     constexpr int A_DMA = MT;                  // activation DMAs per wave per stage: 32 MT rows of 128 bytes
-    constexpr int D = A_DMA + F::C_DMA + F::S_DMA;
-    static_assert(NS >= 2 && NS * F::STAGE <= LDS_MAX, "ring depth / size");
+    // SIDE8: the scales and offsets arrive once per 8 stages (below), not with every stage
+    constexpr int STAGE = SIDE8 ? F::A_BYTES + F::C_BYTES : F::STAGE;
+    constexpr int D = A_DMA + F::C_DMA + (SIDE8 ? 0 : F::S_DMA);
+    static_assert(NS >= 2 && NS * STAGE + (SIDE8 ? wq::SIDE8_BYTES : 0) <= LDS_MAX, "ring depth / size");
     static_assert(MT >= 1 && MT * 32 <= F::BM, "row blocks");
     constexpr int A_BYTES = F::A_BYTES;
     const GroupedArgs& a = ta.a;
@@ -532,7 +548,7 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
     }
 
     auto issue = [&](int kt) {
-        char* st = smem + (kt % NS) * F::STAGE;
+        char* st = smem + (kt % NS) * STAGE;
         const char* ab = (const char*)(a_base + kt * BKD);
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
@@ -548,17 +564,32 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
         char* sst = st + A_BYTES + F::C_BYTES + wave * 256;
         if constexpr (WQ == WQ_F8) {
             __builtin_amdgcn_global_load_lds((const void*)(fs_ptr + (kt >> 1)), DSMOE_LDS_PTR(sst), 4, 0, 0);
-        } else {
+        } else if constexpr (!SIDE8) {
             const int32_t e = (nq + kt) >> 1;
             __builtin_amdgcn_global_load_lds((const void*)(qs_ptr + e), DSMOE_LDS_PTR(sst), 4, 0, 0);
             __builtin_amdgcn_global_load_lds((const void*)(qb_ptr + e), DSMOE_LDS_PTR(sst + 1024), 4, 0, 0);
+        }
+    };
+    // SIDE8: chunk c holds, for every weight row of the tile, the bf16 scales and offsets of
+    // groups [8c, 8c + 8) (stages 8c .. 8c + 7): 16 bytes per row and kind, so lane l of wave w
+    // fetches the 16 bytes of row 64 w + l with one instruction per kind.  Two chunk slots follow
+    // the stage ring: [slot][scale, offset][256 rows][8 groups].  (Needs KD / 64 to be a multiple
+    // of 8, so the 16-byte pieces are aligned and no chunk runs past a row.)
+    char* side8 = smem + NS * STAGE;
+    auto issue_side = [&](int c) {
+        if constexpr (SIDE8) {
+            char* d = side8 + (c & 1) * (wq::SIDE8_BYTES / 2) + wave * 1024;
+            const bf16_t* sb = (const bf16_t*)qs_ptr + nq + 8 * c;  // element (srow, group 8c)
+            const bf16_t* bb = (const bf16_t*)qb_ptr + nq + 8 * c;
+            __builtin_amdgcn_global_load_lds((const void*)sb, DSMOE_LDS_PTR(d), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)bb, DSMOE_LDS_PTR(d + wq::SIDE8_BYTES / 4), 16, 0, 0);
         }
     };
 
     // this lane's codes and scales of stage kt, from LDS
     using BS = BStage<WQ>;
     auto read_b = [&](int kt, BS& bs) {
-        const char* st = smem + (kt % NS) * F::STAGE;
+        const char* st = smem + (kt % NS) * STAGE;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int rho = wave * 64 + j * 32 + (lane & 31);
@@ -569,6 +600,11 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
                 bs.q[j][0] = *(const u32x4*)(row + (((2 * half) ^ sw) << 4));
                 bs.q[j][1] = *(const u32x4*)(row + (((2 * half + 1) ^ sw) << 4));
                 bs.s[j] = *(const float*)side;
+            } else if constexpr (SIDE8) {
+                bs.q[j] = *(const u32x4*)(row + ((half ^ sw) << 4));
+                const char* sd = side8 + ((kt >> 3) & 1) * (wq::SIDE8_BYTES / 2) + rho * 16 + (kt & 7) * 2;
+                bs.s[j] = 512.0f * bf16_to_f32(*(const bf16_t*)sd);  // dequant8 takes 512 s
+                bs.b[j] = bf16_to_f32(*(const bf16_t*)(sd + wq::SIDE8_BYTES / 4));
             } else {
                 bs.q[j] = *(const u32x4*)(row + ((half ^ sw) << 4));
                 // the row's element for this stage is (its group index + kt); odd ones are the
@@ -590,7 +626,7 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
     bf16x8 fa[2][MT], fb[2][2];
     // operands of step s of stage kt: activations from LDS, weights dequantised from registers
     auto frags = [&](int kt, int s, int buf, const BS& bs) {
-        const char* st = smem + (kt % NS) * F::STAGE;
+        const char* st = smem + (kt % NS) * STAGE;
         const int c = 4 * half + s;
 #pragma unroll
         for (int i = 0; i < MT; ++i) fa[buf][i] = as_bf16x8(*(const u32x4*)(st + off(i * 32 + (lane & 31), c)));
@@ -620,7 +656,9 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
     // issued during stage kt-1) has landed: stage kt+1 is complete in LDS, and every wave is done
     // with stage kt's slot, which then receives stage kt+NS.  Past the last stage the DMA repeats
     // stage nk-1 into its own slot (the same bytes; never consumed), so every path issues the
-    // same sequence and the counts stay exact.
+    // same sequence and the counts stay exact.  (Reading the next stage's codes into a second
+    // register set ahead of the barrier, from the wave's own DMAs, measured slower: the compiler
+    // then waited on each of those reads in turn.)
     BS bs;
     auto stage = [&](int kt) {
         frags(kt, 1, 1, bs);
@@ -631,12 +669,17 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
         mfma_step(0);
         wait_vm_barrier<(NS - 2) * D>();
         issue(kt + NS < nk ? kt + NS : nk - 1);
+        // SIDE8: chunk c + 1 goes into the slot of chunk c - 1 (this wave read it last at stage
+        // 8c - 2), 7 stages before it is read; issued after the stage's D operations, so the
+        // waits above stay exact for the stages (they only wait a little earlier for two of them)
+        if (SIDE8 && (kt & 7) == 0 && kt + 8 < nk) issue_side((kt >> 3) + 1);
         const int kn = kt + 1 < nk ? kt + 1 : nk - 1;
         read_b(kn, bs);
         frags(kn, 0, 0, bs);
         mfma_step(1);
     };
 
+    issue_side(0);  // oldest of the prologue's operations, so the wait below covers it
 #pragma unroll
     for (int j = 0; j < NS; ++j) issue(j < nk ? j : nk - 1);
     wait_vm_barrier<(NS - 1) * D>();
@@ -652,27 +695,48 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
         for (int j = 0; j < 2; ++j)
             if (i | j) asm volatile("" : "+a"(acc[i][j]));
 
+    // Epilogue through an LDS image of the output tile, as in gemm_dma: each lane writes its bf16
+    // results -- GEMM-1: bf16(silu(gate) * up), 32 output columns per wave; GEMM-2: 64 -- into a
+    // row-major image (chunk c of row r at c ^ (4 (r / 4 mod 2)), so the two rows one
+    // ds_write_b16 covers fall in different banks), then every thread copies 16-byte row pieces
+    // out.  The ring is reused for the image once every wave's DMAs have landed (the loop's tail
+    // repeats the last stage's DMA) and every wave is past its last LDS read.
+    constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
+    constexpr int RB = OUT_COLS * 2;   // bytes per image row
+    constexpr int OCPR = OUT_COLS / 8;  // 16-byte chunks per image row
+    constexpr int NT = 256;             // threads of the workgroup
+    static_assert(MT * 32 * RB <= wq::lds_bytes(WQ, SWIGLU, SIDE8), "output image exceeds the LDS allocation");
+    auto cswz = [](int r) { return ((r >> 2) & 1) << 2; };
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int rgrp = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
-            const int32_t col = wcol(j, lane & 31);
-            if (col >= N) continue;
+            const int col = SWIGLU ? wave * 32 + (lane & 31) : wave * 64 + j * 32 + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int32_t rr = m0 + i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                if (rr >= cnt) continue;
-                if (SWIGLU)
-                    ((bf16_t*)a.h)[(int64_t)(r0 + rr) * a.ldh + col] =
-                        f32_to_bf16(silu_f(acc[i][0][v]) * acc[i][1][v]);
-                else
-                    ((bf16_t*)a.o)[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[i][j][v]);
+                const int row = i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
+                const float val = SWIGLU ? silu_f(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
+                *(bf16_t*)(smem + row * RB + ((((col >> 3) ^ cswz(row)) << 4) | ((col & 7) << 1))) = f32_to_bf16(val);
             }
         }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    bf16_t* dst = SWIGLU ? (bf16_t*)a.h : (bf16_t*)a.o;
+    const int64_t ld = SWIGLU ? a.ldh : a.H;
+    const int32_t rows = min(cnt - m0, MT * 32);
+#pragma unroll
+    for (int k = 0; k < (MT * 32 * OCPR + NT - 1) / NT; ++k) {
+        const int q = tid + k * NT;
+        const int row = q / OCPR, c = q % OCPR;
+        const int32_t col = n0 + c * 8;
+        if (row >= rows || col >= N) continue;
+        const u32x4 v = *(const u32x4*)(smem + row * RB + ((c ^ cswz(row)) << 4));
+        *(u32x4*)(dst + (int64_t)(r0 + m0 + row) * ld + col) = v;
+    }
 }
 
-template <int WQ, bool SWIGLU>
+template <int WQ, bool SWIGLU, bool SIDE8>
 __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const GroupedArgs& a = ta.a;
@@ -690,20 +754,20 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     const int32_t rows = min(cnt - m0, (int32_t)BM);
     const int32_t q32 = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
     if constexpr (BM == 256) {
-        if (q32 >= 8) wq_tile<WQ, SWIGLU, 8>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 7) wq_tile<WQ, SWIGLU, 7>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 6) wq_tile<WQ, SWIGLU, 6>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 5) wq_tile<WQ, SWIGLU, 5>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 4) wq_tile<WQ, SWIGLU, 4>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 3) wq_tile<WQ, SWIGLU, 3>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 2) wq_tile<WQ, SWIGLU, 2>(ta, smem, g, m0, r0, cnt, n0);
-        else wq_tile<WQ, SWIGLU, 1>(ta, smem, g, m0, r0, cnt, n0);
+        if (q32 >= 8) wq_tile<WQ, SWIGLU, SIDE8, 8>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 7) wq_tile<WQ, SWIGLU, SIDE8, 7>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 6) wq_tile<WQ, SWIGLU, SIDE8, 6>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 5) wq_tile<WQ, SWIGLU, SIDE8, 5>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 4) wq_tile<WQ, SWIGLU, SIDE8, 4>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 3) wq_tile<WQ, SWIGLU, SIDE8, 3>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 2) wq_tile<WQ, SWIGLU, SIDE8, 2>(ta, smem, g, m0, r0, cnt, n0);
+        else wq_tile<WQ, SWIGLU, SIDE8, 1>(ta, smem, g, m0, r0, cnt, n0);
     } else {
         static_assert(BM == 128, "tile height");
-        if (q32 >= 4) wq_tile<WQ, SWIGLU, 4>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 3) wq_tile<WQ, SWIGLU, 3>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 2) wq_tile<WQ, SWIGLU, 2>(ta, smem, g, m0, r0, cnt, n0);
-        else wq_tile<WQ, SWIGLU, 1>(ta, smem, g, m0, r0, cnt, n0);
+        if (q32 >= 4) wq_tile<WQ, SWIGLU, SIDE8, 4>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 3) wq_tile<WQ, SWIGLU, SIDE8, 3>(ta, smem, g, m0, r0, cnt, n0);
+        else if (q32 == 2) wq_tile<WQ, SWIGLU, SIDE8, 2>(ta, smem, g, m0, r0, cnt, n0);
+        else wq_tile<WQ, SWIGLU, SIDE8, 1>(ta, smem, g, m0, r0, cnt, n0);
     }
 }
 
@@ -760,11 +824,11 @@ hipError_t launch_dma_t(const TileArgs& ta, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int WQ, bool SW>
+template <int WQ, bool SW, bool SIDE8 = false>
 hipError_t launch_dma_wq_t(const TileArgs& ta, hipStream_t s) {
-    const size_t lds = (size_t)wq::ring_bytes(WQ);
+    const size_t lds = (size_t)wq::lds_bytes(WQ, SW, SIDE8);
     const unsigned grid = (unsigned)(((ta.nwg + 7) / 8) * 8);
-    hipLaunchKernelGGL((gemm_dma_wq<WQ, SW>), dim3(grid), dim3(THREADS), lds, s, ta);
+    hipLaunchKernelGGL((gemm_dma_wq<WQ, SW, SIDE8>), dim3(grid), dim3(THREADS), lds, s, ta);
     return hipGetLastError();
 }
 
@@ -779,8 +843,10 @@ int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM) {
 // largest dynamic LDS any tiled kernel of this tile height uses
 int32_t tiled_lds_bytes(int32_t BM) {
     int32_t r = dma::ring_bytes(BM);
-    if (BM == wq::bm(WQ_F8)) r = max(r, wq::ring_bytes(WQ_F8));
-    if (BM == wq::bm(WQ_Q4)) r = max(r, wq::ring_bytes(WQ_Q4));
+    if (BM == wq::bm(WQ_F8)) r = max(r, max(wq::lds_bytes(WQ_F8, true), wq::lds_bytes(WQ_F8, false)));
+    if (BM == wq::bm(WQ_Q4))
+        r = max(r, max(max(wq::lds_bytes(WQ_Q4, true), wq::lds_bytes(WQ_Q4, false)),
+                       max(wq::lds_bytes(WQ_Q4, true, true), wq::lds_bytes(WQ_Q4, false, true))));
     return r;
 }
 
@@ -791,11 +857,13 @@ hipError_t configure_tiled_kernels() {
     const void* ks[] = {
         (const void*)gemm_dma<256, true>,           (const void*)gemm_dma<256, false>,
         (const void*)gemm_dma<128, true>,           (const void*)gemm_dma<128, false>,
-        (const void*)gemm_dma_wq<WQ_Q4, true>,      (const void*)gemm_dma_wq<WQ_Q4, false>,
-        (const void*)gemm_dma_wq<WQ_F8, true>,      (const void*)gemm_dma_wq<WQ_F8, false>,
+        (const void*)gemm_dma_wq<WQ_Q4, true, false>,  (const void*)gemm_dma_wq<WQ_Q4, false, false>,
+        (const void*)gemm_dma_wq<WQ_Q4, true, true>,   (const void*)gemm_dma_wq<WQ_Q4, false, true>,
+        (const void*)gemm_dma_wq<WQ_F8, true, false>,  (const void*)gemm_dma_wq<WQ_F8, false, false>,
     };
-    const int bms[] = {256, 256, 128, 128, wq::bm(WQ_Q4), wq::bm(WQ_Q4), wq::bm(WQ_F8), wq::bm(WQ_F8)};
-    for (int i = 0; i < 8; ++i) {
+    const int bms[] = {256, 256, 128, 128, wq::bm(WQ_Q4), wq::bm(WQ_Q4), wq::bm(WQ_Q4), wq::bm(WQ_Q4),
+                       wq::bm(WQ_F8), wq::bm(WQ_F8)};
+    for (int i = 0; i < 10; ++i) {
         hipError_t e = hipFuncSetAttribute(ks[i], hipFuncAttributeMaxDynamicSharedMemorySize, tiled_lds_bytes(bms[i]));
         if (e != hipSuccess) return e;
     }
@@ -829,7 +897,13 @@ hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32
     // quantised layers use the tile height of their format (plan_tiles)
     if (BM != tiled_quant_bm(wdt)) return hipErrorInvalidValue;
     if (wdt == MOE_FP8) return gemm1 ? launch_dma_wq_t<WQ_F8, true>(ta, s) : launch_dma_wq_t<WQ_F8, false>(ta, s);
-    if (wdt == MOE_Q4G64) return gemm1 ? launch_dma_wq_t<WQ_Q4, true>(ta, s) : launch_dma_wq_t<WQ_Q4, false>(ta, s);
+    if (wdt == MOE_Q4G64) {
+        // scales and offsets in chunks of 8 groups when the reduction length allows it
+        const int32_t KD = gemm1 ? a.H : a.I;
+        if (KD % 512 == 0)
+            return gemm1 ? launch_dma_wq_t<WQ_Q4, true, true>(ta, s) : launch_dma_wq_t<WQ_Q4, false, true>(ta, s);
+        return gemm1 ? launch_dma_wq_t<WQ_Q4, true>(ta, s) : launch_dma_wq_t<WQ_Q4, false>(ta, s);
+    }
     return hipErrorInvalidValue;
 }
 

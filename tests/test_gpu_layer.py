@@ -140,6 +140,9 @@ EDGE = [
     ("tiled_q4", C1.with_(T=400, H=512, I=256, Is=192, expert="q4", planted=0)),
     ("tiled_rows256", C1.with_(T=2048, H=256, I=128, Is=128, planted=0)),
     ("tiled_rows256_q4", C1.with_(T=2048, H=256, I=128, Is=128, expert="q4", planted=0)),
+    # reduction lengths that are multiples of 512: the 4-bit kernel takes the scales and offsets in
+    # chunks of 8 groups (two chunks in gate/up, one in down)
+    ("tiled_q4_side_chunks", C1.with_(T=600, H=1024, I=512, Is=256, expert="q4", planted=0)),
     ("tiled_1024_experts_shared", C1.with_(T=100, H=128, I=64, Is=64, E=1024, K=2, G=1, TG=1, planted=0)),
     ("tiled_skewed", C1.with_(T=1500, H=192, I=128, Is=64, zipf_s=2.0, planted=0)),
     # softmax gate and sigmoid-gated shared expert
@@ -271,7 +274,7 @@ SIZES_256 = [1, 33, 64, 65, 96, 0, 128, 129, 160, 161, 200, 0, 250, 256, 257, 30
 SIZES_128 = [1, 40, 64, 65, 80, 0, 96, 97, 127, 128, 129, 0, 150, 200, 255, 256, 300, 412]
 
 
-def exact_group_case(sizes, K, expert):
+def exact_group_case(sizes, K, expert, H=256, I=128):
     """A layer whose routing puts exactly sizes[e] rows in group e: the router is the identity on
     the first E input columns and token t carries 4.0 in the columns of its K experts (0 in the
     other routing columns, N(0,1) elsewhere), so its K largest logits are exactly those experts."""
@@ -280,7 +283,7 @@ def exact_group_case(sizes, K, expert):
     assert TK % K == 0
     T = TK // K
     assert max(sizes) <= T
-    w = C1.with_(T=T, H=256, E=E, K=K, G=1, TG=1, I=128, Is=64, expert=expert, planted=0)
+    w = C1.with_(T=T, H=H, E=E, K=K, G=1, TG=1, I=I, Is=64, expert=expert, planted=0)
     slots = np.repeat(np.arange(E), sizes)          # expert of each slot, expert-major
     chosen = slots.reshape(K, T).T                    # token t: slots t, t + T, ..., distinct experts
     x = synth.normal_bf16(w.seed, 1, T * w.H).reshape(T, w.H)
@@ -292,11 +295,12 @@ def exact_group_case(sizes, K, expert):
     return w, r, b, x, synth.gen_expert_weights(w), synth.gen_shared(w), None
 
 
-@pytest.mark.parametrize("sizes,expert", [(SIZES_256, "bf16"), (SIZES_128, "bf16"), (SIZES_256, "q4"),
-                                          (SIZES_128, "fp8"), (SIZES_256, "fp8")],
-                         ids=["bf16_tiles256", "bf16_tiles128", "q4", "fp8", "fp8_tall_groups"])
-def test_layer_exact_group_sizes(sizes, expert):
-    w, r, b, x, ex, sh, off = exact_group_case(sizes, 4, expert)
+@pytest.mark.parametrize("sizes,expert,H,I", [(SIZES_256, "bf16", 256, 128), (SIZES_128, "bf16", 256, 128),
+                                              (SIZES_256, "q4", 256, 128), (SIZES_256, "q4", 1024, 512),
+                                              (SIZES_128, "fp8", 256, 128), (SIZES_256, "fp8", 256, 128)],
+                         ids=["bf16_tiles256", "bf16_tiles128", "q4", "q4_side_chunks", "fp8", "fp8_tall_groups"])
+def test_layer_exact_group_sizes(sizes, expert, H, I):
+    w, r, b, x, ex, sh, off = exact_group_case(sizes, 4, expert, H, I)
     log(f"[groups] {expert}: T={w.T} sizes {sizes}")
     y, gi, gs = run_small(w, r, b, x, ex, sh, off)
     y_ref, oi, os_, _ = oracle.forward_workload(w, x, r, b, ex, sh, offset=off,
