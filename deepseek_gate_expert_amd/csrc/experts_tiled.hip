@@ -127,6 +127,12 @@ constexpr int LDS_MAX = 160 * 1024;
 constexpr int THREADS = 512;   // 8 waves, two per SIMD
 constexpr int PRODUCERS = 4;   // waves 0..3 issue the DMA, one per SIMD
 constexpr int ring_bytes(int bm) { return NST * (bm + 256) * ROWB; }
+// after the ring: each producer lane's DMA source offsets (A and B, up to 8 each), kept in LDS
+// rather than in 16 registers (one ds_read_b128 per four offsets at each stage's issue; this
+// lowers the kernel's register count by about 10 and measured no slower);
+// [producer][A 0..3, A 4..7, B 0..3, B 4..7][lane] 16-byte groups
+constexpr int OFFS_BYTES = 4 * 4 * 64 * 16;
+constexpr int lds_bytes(int bm) { return ring_bytes(bm) + OFFS_BYTES; }
 // chunk swizzle: the 8 chunks of row r are permuted by (r ^ r/8) mod 8, which keeps the MFMA
 // operand reads free of bank conflicts whether a ds_read_b128 phase serves 8 lanes (rows r..r+7)
 // or 16 lanes (rows r..r+15)
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
     constexpr int A_DMA = A_BYTES / 1024 / PRODUCERS;  // DMA instructions per producer wave per stage
     constexpr int B_DMA = B_BYTES / 1024 / PRODUCERS;
     constexpr int D = A_DMA + B_DMA;
-    static_assert(ring_bytes(BM) <= LDS_MAX, "ring exceeds LDS");
+    static_assert(lds_bytes(BM) <= LDS_MAX && A_DMA <= 8 && B_DMA <= 8, "ring exceeds LDS");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const GroupedArgs& a = ta.a;
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
     // ---- DMA sources: instruction j of producer pw fills LDS rows [8 (pw*X + j), +8); lane i
     // writes chunk i % 8 of row i / 8, so it fetches the logical chunk that the swizzle puts there
     const bf16_t* a_base = SWIGLU ? (const bf16_t*)a.x : (const bf16_t*)a.h;
-    uint32_t a_off[A_DMA];
+    uint32_t a_off[8], b_off[8];
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int r = (pw * A_DMA + j) * 8 + (lane >> 3);
@@ -257,7 +263,6 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
             wb0 = wb1 = shared ? (const bf16_t*)a.swd : (const bf16_t*)a.wd + eoff * KD;
         }
     }
-    uint32_t b_off[B_DMA];
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
         const int br = (pw * B_DMA + j) * 8 + (lane >> 3);
@@ -265,6 +270,15 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
         int32_t n = n0 + (SWIGLU ? br % (NB / 2) : br);
         n = n < N ? n : N - 1;  // columns past N are computed, never stored
         b_off[j] = ((uint32_t)n * (uint32_t)KD + c * 8) * 2u;
+    }
+    // the offsets live in LDS between stages (each lane reads back only what it wrote)
+    u32x4* offs = (u32x4*)(smem + ring_bytes(BM)) + pw * 4 * 64 + lane;
+    if (wave < PRODUCERS) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            offs[q * 64] = u32x4{a_off[4 * q], a_off[4 * q + 1], a_off[4 * q + 2], a_off[4 * q + 3]};
+            offs[(2 + q) * 64] = u32x4{b_off[4 * q], b_off[4 * q + 1], b_off[4 * q + 2], b_off[4 * q + 3]};
+        }
     }
     // a wave's B instruction j covers 8 rows, all gate or all up (NB/2 is a multiple of 8)
     // DMA sources are a uniform base (advanced by the stage) plus a per-lane 32-bit byte offset,
@@ -274,6 +288,16 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
         char* st = smem + (kt % NST) * ST_BYTES;
         const int32_t k0 = kt * BKD;
         const char* ab = (const char*)(a_base + k0);
+        uint32_t a_off[8], b_off[8];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const u32x4 va = offs[q * 64], vb = offs[(2 + q) * 64];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a_off[4 * q + e] = va[e];
+                b_off[4 * q + e] = vb[e];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
             __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[j]),
@@ -818,7 +842,7 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
 
 template <int BM, bool SW>
 hipError_t launch_dma_t(const TileArgs& ta, hipStream_t s) {
-    const size_t lds = (size_t)dma::ring_bytes(BM);
+    const size_t lds = (size_t)dma::lds_bytes(BM);
     const unsigned grid = (unsigned)(((ta.nwg + 7) / 8) * 8);
     hipLaunchKernelGGL((gemm_dma<BM, SW>), dim3(grid), dim3(dma::THREADS), lds, s, ta);
     return hipGetLastError();
@@ -842,7 +866,7 @@ int32_t tiled_max_tiles(int64_t T, int32_t K, int32_t E, int32_t BM) {
 
 // largest dynamic LDS any tiled kernel of this tile height uses
 int32_t tiled_lds_bytes(int32_t BM) {
-    int32_t r = dma::ring_bytes(BM);
+    int32_t r = dma::lds_bytes(BM);
     if (BM == wq::bm(WQ_F8)) r = max(r, max(wq::lds_bytes(WQ_F8, true), wq::lds_bytes(WQ_F8, false)));
     if (BM == wq::bm(WQ_Q4))
         r = max(r, max(max(wq::lds_bytes(WQ_Q4, true), wq::lds_bytes(WQ_Q4, false)),
