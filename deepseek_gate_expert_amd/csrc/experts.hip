@@ -11,12 +11,12 @@
 // This file holds the weight-streaming kernel ("stream"), for groups of up to 64 rows -- the
 // decode regime, where the layer is bound by HBM bandwidth.  A workgroup of four wavefronts
 // owns 64 output columns of one group; each wavefront owns 16 of them and reads its weight
-// rows from HBM exactly once per 64-row chunk of the group, straight into registers, one
-// 128-element step ahead of the MFMAs that consume them.  The activation rows of the chunk
-// (gathered x rows for GEMM-1, h rows for GEMM-2) are shared by the four wavefronts: each step
-// they are copied by LDS DMA into one of two 16 KB LDS buffers, one step ahead, so every
-// activation byte leaves L2 once per workgroup and the loads of a step are waited for with a
-// single count and barrier.  A step feeds four v_mfma_f32_16x16x32_bf16 per 16-row block (gate
+// rows from HBM exactly once per 64-row chunk of the group, straight into registers, two
+// 128-element steps ahead of the MFMAs that consume them (three for fp8 and for the bf16 down
+// projection).  The activation rows of the chunk (gathered x rows for GEMM-1, h rows for
+// GEMM-2) are shared by the four wavefronts: they are copied by LDS DMA into a ring of three
+// 16 KB LDS buffers, two steps ahead, so every activation byte leaves L2 once per workgroup and
+// the loads of a step are waited for with a single count and barrier.  A step feeds four v_mfma_f32_16x16x32_bf16 per 16-row block (gate
 // and up each for GEMM-1).  The k index inside a step is permuted identically for both
 // operands (KLayout), so the sum is unchanged.
 // MFMA 16x16x32 bf16 operand layout: lane l supplies row/column (l % 16) and eight
