@@ -400,14 +400,14 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 
 
 // ---------------------------------------------------------------------------------------------
-// Quantised weights: 4-bit (affine, groups of 64 along the reduction axis; tiles of 256 rows)
-// or fp8 (OCP E4M3 codes, one fp32 scale per 128 x 128 block; tiles of 128 rows), 256 weight
-// rows per tile, same tile list as gemm_dma.  A tile computes only its real rows rounded up to
+// Quantised weights: 4-bit (affine, groups of 64 along the reduction axis) or fp8 (OCP E4M3
+// codes, one fp32 scale per 128 x 128 block), tiles of 128 rows x 256 weight rows, same tile list
+// as gemm_dma.  A tile computes only its real rows rounded up to
 // 32 (a variant per height), while its weights are staged and dequantised once whatever its
 // height.  Every operand of a 64-k stage -- the activation rows, the weight codes and the
-// scales (and 4-bit offsets) -- enters LDS by DMA, in a ring of stages (three for 4-bit, two
-// for fp8: stages up to kt+NS-1 in flight while kt is computed).  With no register loads in the loop the compiler inserts
-// no waits of its own: the only waits are the explicit count + barrier per stage.  (Loading the
+// scales (and 4-bit offsets) -- enters LDS by DMA, in a ring of two stages (stage kt+1 in flight
+// while kt is computed).  With no register loads in the loop the compiler inserts no waits of
+// its own: the only waits are the explicit count + barrier per stage.  (Loading the
 // codes into registers beside an LDS DMA ring made the compiler wait for every outstanding load
 // before each use of them, which exposed the full memory latency once per stage.)
 // The dequantisation -- bf16(s*q + b), resp. bf16(value * scale) -- runs on the vector ALU
@@ -431,16 +431,18 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 enum { WQ_Q4 = 0, WQ_F8 = 1 };
 
 namespace wq {
-// rows of the tile list's tiles: 256 for 4-bit (one workgroup per CU; its dequantisation is the
-// costlier one, so halving it per row pays for the lost second workgroup), 128 for fp8 (two
-// workgroups of 66 KB share a CU)
-constexpr int bm(int wqt) { return wqt == WQ_F8 ? 128 : 256; }
+// rows of the tile list's tiles: 128 for both formats, so two workgroups (64 KB of LDS and two
+// waves per SIMD between them) share a CU and one's dequantisation runs under the other's
+// MFMAs.  (256-row 4-bit tiles -- one workgroup per CU, each weight dequantised once per 256
+// rows -- measured about 2 % slower on the DeepSeek-V3 4-bit prefill layer, T = 4096, whose
+// groups average about 150 rows.)
+constexpr int bm(int) { return 128; }
 template <int WQ>
 struct Fmt {
     static constexpr int BM = bm(WQ);
     static constexpr int A_BYTES = BM * dma::ROWB;              // activation slot of one stage
-    // ring depth: three stages for 4-bit (126 KB), two for fp8 (66 KB)
-    static constexpr int NS = WQ == WQ_F8 ? 2 : 3;
+    // ring depth: two stages (4-bit: 52 KB, or 48 KB plus 16 KB of chunked side data; fp8: 66 KB)
+    static constexpr int NS = 2;
     static constexpr int CB = WQ == WQ_F8 ? 64 : 32;            // code bytes per weight row per stage
     static constexpr int ROWS_PER_DMA = 1024 / CB;              // weight rows per DMA instruction
     static constexpr int C_DMA = 64 / ROWS_PER_DMA;             // code DMAs per wave per stage
@@ -777,22 +779,11 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     constexpr int BM = wq::bm(WQ);
     const int32_t rows = min(cnt - m0, (int32_t)BM);
     const int32_t q32 = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
-    if constexpr (BM == 256) {
-        if (q32 >= 8) wq_tile<WQ, SWIGLU, SIDE8, 8>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 7) wq_tile<WQ, SWIGLU, SIDE8, 7>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 6) wq_tile<WQ, SWIGLU, SIDE8, 6>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 5) wq_tile<WQ, SWIGLU, SIDE8, 5>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 4) wq_tile<WQ, SWIGLU, SIDE8, 4>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 3) wq_tile<WQ, SWIGLU, SIDE8, 3>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 2) wq_tile<WQ, SWIGLU, SIDE8, 2>(ta, smem, g, m0, r0, cnt, n0);
-        else wq_tile<WQ, SWIGLU, SIDE8, 1>(ta, smem, g, m0, r0, cnt, n0);
-    } else {
-        static_assert(BM == 128, "tile height");
-        if (q32 >= 4) wq_tile<WQ, SWIGLU, SIDE8, 4>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 3) wq_tile<WQ, SWIGLU, SIDE8, 3>(ta, smem, g, m0, r0, cnt, n0);
-        else if (q32 == 2) wq_tile<WQ, SWIGLU, SIDE8, 2>(ta, smem, g, m0, r0, cnt, n0);
-        else wq_tile<WQ, SWIGLU, SIDE8, 1>(ta, smem, g, m0, r0, cnt, n0);
-    }
+    static_assert(BM == 128, "tile height");
+    if (q32 >= 4) wq_tile<WQ, SWIGLU, SIDE8, 4>(ta, smem, g, m0, r0, cnt, n0);
+    else if (q32 == 3) wq_tile<WQ, SWIGLU, SIDE8, 3>(ta, smem, g, m0, r0, cnt, n0);
+    else if (q32 == 2) wq_tile<WQ, SWIGLU, SIDE8, 2>(ta, smem, g, m0, r0, cnt, n0);
+    else wq_tile<WQ, SWIGLU, SIDE8, 1>(ta, smem, g, m0, r0, cnt, n0);
 }
 
 // Tile list (offsets is read only for routed groups: it may be NULL when E == 0): every group in
