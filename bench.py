@@ -39,6 +39,7 @@ METRIC = "MoE-layer tokens/sec (DeepSeek-V3 shape, bf16) + % HBM/MFMA peak"
 TRAFFIC_PROFILES = {
     "c3": ("gemm_dma_gate_up_dsv3_prefill_T8192_hbm_traffic.md", "experts_tiled.hip"),
     "c2": ("stream_gemm_gate_up_dsv3_decode_T64_hbm_traffic.md", "experts.hip"),
+    "c4": ("gemm_dma_wq_q4_dsv3_T4096_traffic.md", "experts_tiled.hip"),
 }
 
 
