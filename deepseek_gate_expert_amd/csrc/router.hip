@@ -175,7 +175,10 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, c
 // through).  So each wave first touches, with loads spread over its lanes, its whole expert row
 // (16 loads of 1 KB) and one slice of the 64 token rows: waves of one block that share an XCD
 // (expert ids congruent mod 8, with E a multiple of 8) split those rows between them.  The
-// values are discarded; the ring then hits in cache.
+// values are discarded; the ring then hits in cache.  All twenty touching loads are issued
+// before any is waited for (lanes past a row's end re-touch its last line), so they cost about
+// one memory latency: loading them under per-lane conditions made the compiler wait for each in
+// turn (67 against 61 us for the DeepSeek-V3 decode batch, T = 64).
 constexpr int GV_CK = 32;
 
 template <typename TA>
@@ -185,10 +188,12 @@ __device__ __forceinline__ uint32_t warm_rows(const TA* x, const TA* wr, int64_t
     if (H % 8 != 0 || E < 64 || (E & 7) != 0) return sink;  // 16-byte aligned rows; 8+ waves per XCD
     const int64_t wbytes = (int64_t)H * sizeof(TA);
     const char* wb = (const char*)wr;
+    uint32_t got[20];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int64_t o = (int64_t)i * 1024 + lane * 16;
-        if (o + 16 <= wbytes) sink ^= (*(const u32x4*)(wb + o))[0];
+        int64_t o = (int64_t)i * 1024 + lane * 16;
+        o = o + 16 <= wbytes ? o : wbytes - 16;
+        got[i] = *(const uint32_t*)(wb + o);  // one word per lane touches each 128-byte line
     }
     const int64_t t0 = (int64_t)blockIdx.y * 64;
     const int64_t rows = T - t0 < 64 ? T - t0 : 64;
@@ -200,9 +205,13 @@ __device__ __forceinline__ uint32_t warm_rows(const TA* x, const TA* wr, int64_t
     const char* xb = (const char*)(x + t0 * H);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t j = i * 64 + lane, l = l0 + j;
-        if (j < per && l * 128 + 4 <= xbytes) sink ^= *(const uint32_t*)(xb + l * 128);
+        const int64_t j = i * 64 + lane;
+        int64_t l = l0 + (j < per ? j : per - 1);
+        l = l < lines ? l : lines - 1;
+        got[16 + i] = *(const uint32_t*)(xb + l * 128);
     }
+#pragma unroll
+    for (int i = 0; i < 20; ++i) sink ^= got[i];
     return sink;
 }
 
