@@ -26,6 +26,8 @@ ROUTER_SHAPES = [
     (1000, 7168, 256, "bf16"),   # 2x2 register tiles, ragged tokens
     (700, 200, 96, "f32"),       # 2x2, partial last chunk, ragged experts
     (3000, 7168, 1, "bf16"),     # one expert (the shared-expert gate): GEMV at many tokens
+    (37, 7168, 256, "bf16"),     # GEMV, ragged token block: row touching clamped to the block's rows
+    (300, 520, 64, "bf16"),      # GEMV, short rows: every touching lane past a row's end clamped
 ]
 
 
