@@ -150,6 +150,7 @@ inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 // makes concurrent first calls safe.
 constexpr int MAX_DEVICES = 64;
 int g_tiled_state[MAX_DEVICES];
+bool g_stream_dma_ok[MAX_DEVICES];  // the DMA weight-streaming kernels may take their LDS
 std::once_flag g_tiled_once[MAX_DEVICES];
 
 int tiled_state() {
@@ -163,10 +164,20 @@ int tiled_state() {
             if (lds >= tiled_lds_bytes(256)) st = 1;
             else if (lds >= tiled_lds_bytes(128)) st = 2;
         }
+        g_stream_dma_ok[dev] = configure_stream_dma() == hipSuccess;
         (void)hipGetLastError();
         g_tiled_state[dev] = st;
     });
     return g_tiled_state[dev];
+}
+
+// bf16 weight streaming through the LDS DMA ring when the device allows its LDS and the weight
+// offsets fit 32 bits; else the register-streaming kernel
+bool use_stream_dma(const GroupedArgs& a) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return false;
+    tiled_state();
+    return g_stream_dma_ok[dev] && stream_dma_fits(a);
 }
 
 // Dense SwiGLU MLP: the shared-expert path on its own (group E with E = 0 routed experts).
@@ -329,6 +340,7 @@ int launch_forward(const moe_layer_desc* d, const void* x, const void* router_w,
     auto streamed = [&](bool first) -> int {
         if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));
         if (tp.on && tp.min_rows == 0) return MOE_OK;  // every group is tiled
+        if (!quant && use_stream_dma(a)) return hip_rc(launch_stream_dma(a, first, 0, gend, s));
         return hip_rc(first ? launch_gemm1_bf16(a, 0, gend, rdt, s) : launch_gemm2_bf16(a, 0, gend, rdt, s));
     };
     // tiled kernels of one pass (the other groups)
@@ -437,6 +449,10 @@ int moe_dense_mlp(int64_t T, int32_t H, int32_t I, int32_t act_dtype, const void
                        (int64_t)I * H < lim;
     a.stream_max_rows = tiled ? STREAM_MAX_ROWS : 0x7fffffff;
     if (!tiled) {
+        if (use_stream_dma(a)) {
+            if ((rc = hip_rc(launch_stream_dma(a, true, 0, 1, s)))) return rc;
+            return hip_rc(launch_stream_dma(a, false, 0, 1, s));
+        }
         if ((rc = hip_rc(launch_gemm1_bf16(a, 0, 1, MOE_BF16, s)))) return rc;
         return hip_rc(launch_gemm2_bf16(a, 0, 1, MOE_BF16, s));
     }

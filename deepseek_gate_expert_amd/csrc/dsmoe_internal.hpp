@@ -92,6 +92,11 @@ hipError_t launch_dispatch(const int32_t* inds, int64_t T, int32_t K, int32_t E,
 // (MOE_BF16, MOE_Q4G64 or MOE_FP8; the shared group E is always bf16 and may be in the range)
 hipError_t launch_gemm1_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s);
 hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32_t wdt, hipStream_t s);
+// bf16 weights of groups [g0, g1) streamed through an LDS DMA ring (groups of at most
+// stream_max_rows rows); configure once per device before the first launch
+hipError_t configure_stream_dma();
+bool stream_dma_fits(const GroupedArgs& a);
+hipError_t launch_stream_dma(const GroupedArgs& a, bool gemm1, int32_t g0, int32_t g1, hipStream_t s);
 // fp32 layers: all routed rows and the shared rows in one launch each
 hipError_t launch_gemm1_f32(const GroupedArgs& a, hipStream_t s);
 hipError_t launch_gemm2_f32(const GroupedArgs& a, hipStream_t s);
