@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/sec (DeepSeek-V3 shape, bf16) + % HBM/MFMA peak"
 # describes the kernel and "traffic" is null.
 TRAFFIC_PROFILES = {
     "c3": ("gemm_dma_gate_up_dsv3_prefill_T8192_hbm_traffic.md", "experts_tiled.hip"),
-    "c2": ("stream_gemm_gate_up_dsv3_decode_T64_hbm_traffic.md", "experts.hip"),
+    "c2": ("stream_dma_gate_up_dsv3_decode_T64_hbm_traffic.md", "experts_stream.hip"),
     "c4": ("gemm_dma_wq_q4_dsv3_T4096_traffic.md", "experts_tiled.hip"),
 }
 
@@ -353,7 +353,9 @@ def main():
             roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                     "traffic": tr, "traffic_unit": "GB per launch (memory-side reads + writes)",
                     "traffic_source": tr_src,
-                    "kernel": f"stream_gemm<{wl.expert}, gate/up> (weight-streaming gate/up + SwiGLU)"}
+                    "kernel": ("stream_dma<gate/up> (bf16 weights streamed through an LDS DMA ring, gate/up + SwiGLU)"
+                               if wl.expert == "bf16" else
+                               f"stream_gemm<{wl.expert}, gate/up> (weight-streaming gate/up + SwiGLU)")}
             layer = layer_bytes(wl, res["n_hit"]) / (res["step_ms"] / 1e3) / 1e9
             roof["layer_achieved"] = layer
             roof["layer_frac"] = layer / PEAK_HBM_GBS
