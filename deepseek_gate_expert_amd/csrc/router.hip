@@ -6,10 +6,13 @@
 //
 // Every output element is accumulated by one fused multiply-add per k, k ascending, starting
 // from +0.0f, then one fp32 add of the offset.  Because the order is fixed the logits are
-// reproducible bit for bit, which keeps the expert selection stable.  That rules out MFMA
-// (its internal summation order is not specified), so these are VALU kernels in which the k
-// loop of an output is never split across threads and the zero tail of a partial k chunk is
-// never fed to an FMA.
+// reproducible bit for bit, which keeps the expert selection stable.  That rules out the matrix
+// instructions that sum several k inside (their internal order and rounding are not specified),
+// but not the fp32 ones that take a single k (see router_mfma).  In every kernel the k loop of
+// an output is never split across threads and the zero tail of a partial k chunk is never
+// multiplied.
+#include <type_traits>
+
 #include "dsmoe_internal.hpp"
 
 namespace dsmoe {
@@ -57,110 +60,170 @@ __device__ __forceinline__ float raw8_at(const Raw8<TA>& r, int j) {
     else return __uint_as_float(r.q[j >> 2][j & 3]);
 }
 
-// Many tokens: 256 threads, MT x NT register tile per thread (BM = 16 MT tokens x BN = 16 NT
-// experts per workgroup), k chunks of KC staged in LDS as fp32 (k-major), double buffered.  The
-// global loads run RD chunks ahead in a ring of raw registers, so with x coming from HBM (as in
-// a layer) their latency stays hidden.  Full chunks run a fully unrolled k loop, so the LDS
-// reads of later k steps issue ahead of the FMAs.
-constexpr int RD = 3;
+// Many tokens, on the matrix cores.  v_mfma_f32_16x16x1_4b_f32 multiplies four independent
+// 16 x 1 by 1 x 16 fp32 blocks and adds each product to its accumulator: one k per instruction,
+// so every output receives exactly one multiply-add, C + a * b rounded once.  Checked on MI355X
+// against fmaf for about 10^8 operand triples (bf16-valued and general fp32 operands, subnormal,
+// infinite and NaN operands, signed zeros): the same bits in every case.  A chain of these
+// instructions over k ascending, from +0.0f, is therefore the same fixed-order FMA chain as in
+// the VALU kernel, at the matrix cores' fp32 rate (twice the non-packed vector rate).
+//
+// Workgroup: 64 tokens x 64 experts, four waves, wave w owning experts [16 w, 16 w + 16) of the
+// tile for all 64 tokens: A operand lane l = token l (block l / 16 = tokens [16 b, 16 b + 16)),
+// B operand lane l = expert 16 w + l % 16 (the same 16 experts in all four blocks).  Output
+// register r of lane l: block r / 4, token 16 (r / 4) + 4 (l / 16) + r % 4, expert l % 16.
+// Operands are staged as fp32 in LDS, [row][k] with rows padded by four floats so that the
+// 16-byte reads of 16 consecutive rows fall in distinct banks; each 16-byte read supplies four
+// consecutive k.  Three LDS buffers: while chunk c is multiplied, chunk c + 2 is widened into
+// the buffer that chunk c - 1 used, and the first operands of chunk c + 1 (staged during chunk
+// c - 1) are read before the end-of-chunk barrier, so that the barrier, the staging and the LDS
+// latency stay off the matrix pipe's path as far as the schedule allows.  Global loads run
+// RM_RD chunks ahead of the staging in raw registers.  Tiles are ordered so that the expert
+// tiles of one token tile run on one XCD, where they share the token rows in L2.
+constexpr int RM_KC = 32;          // k per staged chunk
+constexpr int RM_LD = RM_KC + 4;   // LDS row stride in floats
+constexpr int RM_NB = 3;           // LDS buffers
+constexpr int RM_RD = 3;           // raw register ring (chunks)
 
-template <typename TA, int MT, int NT, int KC>
-__global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ x, const TA* __restrict__ w,
-                                                     const float* __restrict__ off, float* __restrict__ logits,
-                                                     int64_t T, int32_t H, int32_t E) {
-    constexpr int BM = 16 * MT, BN = 16 * NT;
-    constexpr int LPR = KC / 8;                                     // 8-element loads per row
-    constexpr int XL = BM * LPR / 256, WL = BN * LPR / 256;  // 8-element loads per thread
-    static_assert(XL >= 1 && WL >= 1 && BM * LPR % 256 == 0 && BN * LPR % 256 == 0,
-                  "tile does not fit the staging layout");
-    __shared__ float xs[2][KC][BM + 4];
-    __shared__ float ws[2][KC][BN + 4];
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    const int64_t m0 = (int64_t)blockIdx.x * BM;
-    const int32_t n0 = blockIdx.y * BN;
-    const bool vec = (H % 8) == 0;
-
-    // staging assignment: load i of this thread covers row (tid + 256 i) / LPR, k (tid % LPR) * 8
-    const TA* xrow[XL];
-    const TA* wrow[WL];
-#pragma unroll
-    for (int i = 0; i < XL; ++i) {
-        int64_t t = m0 + (tid + 256 * i) / LPR;
-        xrow[i] = x + (t < T ? t : T - 1) * H;
+template <typename TA, bool VEC>
+__global__ __launch_bounds__(256) void router_mfma(const TA* __restrict__ x, const TA* __restrict__ w,
+                                                   const float* __restrict__ off, float* __restrict__ logits,
+                                                   int64_t T, int32_t H, int32_t E, int32_t ntt, int32_t nte) {
+    __shared__ __attribute__((aligned(16))) float xs[RM_NB][64][RM_LD];
+    __shared__ __attribute__((aligned(16))) float ws[RM_NB][64][RM_LD];
+    // workgroup L runs on XCD L % 8; its position in that XCD's sequence picks the tile
+    const int32_t L = blockIdx.x;
+    const int32_t full = (ntt / 8) * 8 * nte;
+    int32_t tt, te;
+    if (L < full) {
+        const int32_t q = L >> 3;
+        tt = (q / nte) * 8 + (L & 7);
+        te = q % nte;
+    } else {
+        const int32_t r = L - full;
+        tt = (ntt / 8) * 8 + r / nte;
+        te = r % nte;
     }
-#pragma unroll
-    for (int i = 0; i < WL; ++i) {
-        int32_t e = n0 + (tid + 256 * i) / LPR;
-        wrow[i] = w + (int64_t)(e < E ? e : E - 1) * H;
-    }
-    const int kq = (tid % LPR) * 8;
-    Raw8<TA> xq[RD][XL], wq[RD][WL];
+    const int64_t t0 = (int64_t)tt * 64;
+    const int32_t e0 = te * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-    float acc[MT][NT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = 0.0f;
-
-    const int nch = (H + KC - 1) / KC;
+    // staging: thread tid loads 8 k of token row tid / 4 and of expert row tid / 4
+    const int srow = tid >> 2, kq = (tid & 3) * 8;
+    const int64_t st = t0 + srow;
+    const int32_t se = e0 + srow;
+    const TA* xrow = x + (st < T ? st : T - 1) * H;
+    const TA* wrow = w + (int64_t)(se < E ? se : E - 1) * H;
+    Raw8<TA> xq[RM_RD], wq[RM_RD];
+    // With 8-aligned rows (VEC) every load is one unconditional 16-byte vector (two for fp32),
+    // its start clamped to the row's last 8 elements; the k it then covers lie past the row's
+    // end, where the staged values are never multiplied.  (Element loads under per-lane
+    // conditions would make the compiler wait for every load in flight before each staging.)
     auto load = [&](int u, int c) {
+        if constexpr (VEC) {
+            const int32_t i = min(c * RM_KC + kq, H - 8);
 #pragma unroll
-        for (int i = 0; i < XL; ++i) raw8_load(xrow[i], c * KC + kq, H, vec, xq[u][i]);
-#pragma unroll
-        for (int i = 0; i < WL; ++i) raw8_load(wrow[i], c * KC + kq, H, vec, wq[u][i]);
-    };
-#pragma unroll
-    for (int u = 0; u < RD; ++u)
-        if (u < nch) load(u, u);
-    for (int c0 = 0; c0 < nch; c0 += RD) {
-#pragma unroll
-        for (int u = 0; u < RD; ++u) {  // chunk c lives in ring slot c % RD
-            const int c = c0 + u;
-            if (c >= nch) break;
-            const int b = c & 1;
-#pragma unroll
-            for (int i = 0; i < XL; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) xs[b][kq + j][(tid + 256 * i) / LPR] = raw8_at(xq[u][i], j);
-#pragma unroll
-            for (int i = 0; i < WL; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) ws[b][kq + j][(tid + 256 * i) / LPR] = raw8_at(wq[u][i], j);
-            __syncthreads();
-            if (c + RD < nch) load(u, c + RD);
-            auto step = [&](int k) {
-                float a[MT], bb[NT];
-#pragma unroll
-                for (int i = 0; i < MT; ++i) a[i] = xs[b][k][ty * MT + i];
-#pragma unroll
-                for (int j = 0; j < NT; ++j) bb[j] = ws[b][k][tx * NT + j];
-#pragma unroll
-                for (int i = 0; i < MT; ++i)
-#pragma unroll
-                    for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_fmaf(a[i], bb[j], acc[i][j]);
-            };
-            const int kc = min(KC, H - c * KC);  // the zero tail of the last chunk is never used
-            if (kc == KC) {
-#pragma unroll
-                for (int k = 0; k < KC; ++k) step(k);
-            } else {
-                for (int k = 0; k < kc; ++k) step(k);
+            for (int v = 0; v < (int)sizeof(TA) / 2; ++v) {
+                xq[u].q[v] = *(const u32x4*)(xrow + i + v * (16 / (int)sizeof(TA)));
+                wq[u].q[v] = *(const u32x4*)(wrow + i + v * (16 / (int)sizeof(TA)));
             }
-            // buffer b is rewritten two chunks later, after the next chunk's barrier
+        } else {
+            raw8_load(xrow, c * RM_KC + kq, H, false, xq[u]);
+            raw8_load(wrow, c * RM_KC + kq, H, false, wq[u]);
         }
+    };
+    auto stage = [&](int u, int b) {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo[j] = raw8_at(xq[u], j);
+            hi[j] = raw8_at(xq[u], j + 4);
+        }
+        *(f32x4*)&xs[b][srow][kq] = lo;
+        *(f32x4*)&xs[b][srow][kq + 4] = hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo[j] = raw8_at(wq[u], j);
+            hi[j] = raw8_at(wq[u], j + 4);
+        }
+        *(f32x4*)&ws[b][srow][kq] = lo;
+        *(f32x4*)&ws[b][srow][kq + 4] = hi;
+    };
+
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+
+    const int nch = (H + RM_KC - 1) / RM_KC, nfull = H / RM_KC;
+    const int brow = 16 * wv + (lane & 15);
+    // Chunk s is loaded into ring slot s % RM_RD and staged into buffer s % RM_NB.  Loads and
+    // staging run unconditionally (a chunk index past the last one re-reads the last chunk, and
+    // its staging fills a buffer that no later chunk reads), so the number of loads in flight is
+    // the same on every path and the wait before a staging step can leave the later chunks'
+    // loads in flight.
+#pragma unroll
+    for (int u = 0; u < RM_RD; ++u) load(u, min(u, nch - 1));
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0) {
+        stage(s0, s0);
+        load(s0, min(s0 + RM_RD, nch - 1));
     }
+    __syncthreads();
+
+    f32x4 av = *(const f32x4*)&xs[0][lane][0], bv = *(const f32x4*)&ws[0][brow][0];
+    // chunk c (full) from buffer U = c % 3; staging of chunk c + 2 from slot (U + 2) % 3
+    auto chunk = [&](auto U, int c) {
+        constexpr int u = decltype(U)::value;
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int64_t t = m0 + ty * MT + i;
-        if (t >= T) continue;
+        for (int g = 0; g < RM_KC / 4; ++g) {
+            f32x4 an, bn;
+            if (g + 1 < RM_KC / 4) {
+                an = *(const f32x4*)&xs[u][lane][4 * g + 4];
+                bn = *(const f32x4*)&ws[u][brow][4 * g + 4];
+            } else {  // chunk c + 1 was staged during chunk c - 1 (an unused read past the end is harmless)
+                an = *(const f32x4*)&xs[(u + 1) % RM_NB][lane][0];
+                bn = *(const f32x4*)&ws[(u + 1) % RM_NB][brow][0];
+            }
+            if (g == 2) {  // buffer (u + 2) % 3 last held chunk c - 1
+                constexpr int su = (u + 2) % RM_RD;
+                stage(su, (u + 2) % RM_NB);
+                load(su, min(c + 2 + RM_RD, nch - 1));
+            }
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int32_t e = n0 + tx * NT + j;
-            if (e >= E) continue;
-            float v = acc[i][j];
-            if (off) v = v + off[e];
-            logits[t * E + e] = v;
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x1f32(av[j], bv[j], acc, 0, 0, 0);
+            av = an;
+            bv = bn;
         }
+        __syncthreads();  // buffer u is restaged during chunk c + 1; chunk c + 2 becomes visible
+    };
+    // whole triples in the loop (no exit inside an iteration, so every path into the loop has the
+    // same loads in flight), then the remaining full chunks
+    int c0 = 0;
+    for (; c0 + RM_NB <= nfull; c0 += RM_NB) {
+        chunk(std::integral_constant<int, 0>{}, c0);
+        chunk(std::integral_constant<int, 1>{}, c0 + 1);
+        chunk(std::integral_constant<int, 2>{}, c0 + 2);
+    }
+    if (c0 < nfull) chunk(std::integral_constant<int, 0>{}, c0);
+    if (c0 + 1 < nfull) chunk(std::integral_constant<int, 1>{}, c0 + 1);
+    if (nfull < nch) {  // partial last chunk: its zero tail is never used
+        const int b = nfull % RM_NB, kc = H - nfull * RM_KC;
+        for (int k = 0; k < kc; ++k)
+            acc = __builtin_amdgcn_mfma_f32_16x16x1f32(xs[b][lane][k], ws[b][brow][k], acc, 0, 0, 0);
+    }
+    // the accumulators are read right after the last MFMA, possibly behind the tail branch:
+    // issue the MFMA-to-VALU wait states explicitly before any of them is read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+    const int32_t e = e0 + 16 * wv + (lane & 15);
+    if (e >= E) return;
+    const float o = off ? off[e] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int64_t t = t0 + 16 * (r >> 2) + 4 * (lane >> 4) + (r & 3);
+        if (t >= T) continue;
+        float v = acc[r];
+        if (off) v = v + o;
+        logits[t * E + e] = v;
     }
 }
 
@@ -289,25 +352,27 @@ hipError_t launch_gemv(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E
     return hipGetLastError();
 }
 
-template <typename TA, int MT, int NT, int KC>
-hipError_t launch_t(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, const float* off, float* logits,
-                    hipStream_t s) {
-    const dim3 grid((unsigned)((T + 16 * MT - 1) / (16 * MT)), (E + 16 * NT - 1) / (16 * NT));
-    hipLaunchKernelGGL((router_kernel<TA, MT, NT, KC>), grid, dim3(256), 0, s, x, w, off, logits, T, H, E);
+template <typename TA>
+hipError_t launch_mfma(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, const float* off, float* logits,
+                       hipStream_t s) {
+    const int32_t ntt = (int32_t)((T + 63) / 64), nte = (E + 63) / 64;
+    if (H % 8 == 0)
+        hipLaunchKernelGGL((router_mfma<TA, true>), dim3((unsigned)ntt * nte), dim3(256), 0, s, x, w, off, logits, T, H,
+                           E, ntt, nte);
+    else
+        hipLaunchKernelGGL((router_mfma<TA, false>), dim3((unsigned)ntt * nte), dim3(256), 0, s, x, w, off, logits, T,
+                           H, E, ntt, nte);
     return hipGetLastError();
 }
 
-// Few tokens or few experts: one output per lane (GEMV shape).  Otherwise the largest register
-// tile that still gives at least 256 workgroups (one per CU): 4 x 4 (64 x 64 logits per
-// workgroup), then 2 x 4, then 2 x 2 with 64-k chunks.  The summation order is the same in all.
+// Few tokens or few experts: one output per lane (GEMV shape).  Otherwise the matrix-core
+// kernel.  The summation order is the same in both.
 template <typename TA>
 hipError_t route_shape(const TA* x, const TA* w, int64_t T, int32_t H, int32_t E, const float* off,
                        float* logits, hipStream_t s) {
     if (T <= 512 || E < 16) return launch_gemv<TA>(x, w, T, H, E, off, logits, s);
-    const int64_t ecols = (E + 63) / 64;
-    if (((T + 63) / 64) * ecols >= 256) return launch_t<TA, 4, 4, 32>(x, w, T, H, E, off, logits, s);
-    if (((T + 31) / 32) * ecols >= 256) return launch_t<TA, 2, 4, 64>(x, w, T, H, E, off, logits, s);
-    return launch_t<TA, 2, 2, 64>(x, w, T, H, E, off, logits, s);
+    if (((T + 63) / 64) * ((E + 63) / 64) > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+    return launch_mfma<TA>(x, w, T, H, E, off, logits, s);
 }
 
 }  // namespace

@@ -17,14 +17,17 @@ ROUTER_SHAPES = [
     (16, 64, 8, "f32"),
     (512, 1024, 64, "bf16"),
     (64, 7168, 256, "bf16"),
-    (8192, 7168, 256, "bf16"),   # 4x4 register tiles
+    (8192, 7168, 256, "bf16"),   # matrix-core kernel, DeepSeek-V3 prefill shape
     (37, 200, 96, "f32"),        # ragged everywhere, partial k chunk
-    (2049, 96, 1000, "bf16"),    # many experts, ragged tiles
+    (2049, 96, 1000, "bf16"),    # many experts, ragged token and expert tiles
     (1, 7168, 256, "bf16"),
-    (2048, 7168, 256, "bf16"),   # 2x4 register tiles, 64-k chunks
-    (2500, 136, 256, "f32"),     # 2x4, partial last chunk
-    (1000, 7168, 256, "bf16"),   # 2x2 register tiles, ragged tokens
-    (700, 200, 96, "f32"),       # 2x2, partial last chunk, ragged experts
+    (2048, 7168, 256, "bf16"),
+    (2500, 136, 256, "f32"),     # fp32 operands, partial last chunk
+    (1000, 7168, 256, "bf16"),   # ragged tokens
+    (700, 200, 96, "f32"),       # partial last chunk, ragged experts
+    (777, 99, 64, "bf16"),       # rows not a multiple of 8: element loads, partial last chunk
+    (600, 37, 20, "f32"),        # rows not a multiple of 8, one partial chunk, 20 of 64 experts
+    (1030, 24, 48, "bf16"),      # rows shorter than one chunk (only the partial chunk)
     (3000, 7168, 1, "bf16"),     # one expert (the shared-expert gate): GEMV at many tokens
     (37, 7168, 256, "bf16"),     # GEMV, ragged token block: row touching clamped to the block's rows
     (300, 520, 64, "bf16"),      # GEMV, short rows: every touching lane past a row's end clamped
@@ -48,6 +51,36 @@ def test_router_logits_bit_exact(T, H, E, act, with_offset):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
         f"{np.count_nonzero(got != ref)} logits differ, max abs {np.max(np.abs(got - ref))}"
 
+
+
+@pytest.mark.parametrize("T,H,E,act", [(600, 64, 32, "f32"), (40, 64, 32, "f32"), (700, 72, 48, "bf16")])
+def test_router_logits_bit_exact_subnormal(T, H, E, act):
+    """Products and partial sums in the subnormal range, and exact zeros: the matrix-core router
+    (T > 512) and the GEMV (T <= 512) keep the fused multiply-add chain bit for bit there too."""
+    log(f"[router-subnormal] T={T} H={H} E={E} {act}")
+    def gen(tid, n):
+        if act == "f32":
+            return synth.normal_f32(T + H + 7, tid, n, 1.0)
+        return (synth.normal_bf16(T + H + 7, tid, n, 1.0).astype(np.uint32) << 16).view(np.float32)
+    x = gen(1, T * H).reshape(T, H)
+    w = gen(2, E * H).reshape(E, H)
+    x *= np.float32(2.0 ** -70)   # products near 2^-140: below the normal range (2^-126)
+    w *= np.float32(2.0 ** -70)
+    x[:, ::5] = 0.0               # exact zeros, and rows of zeros
+    w[::7, :] = 0.0
+    if act == "bf16":             # scaled by powers of two, so still bf16 values
+        x = x.view(np.uint32)
+        w = w.view(np.uint32)
+        assert not (x & 0xFFFF).any() and not (w & 0xFFFF).any()
+        x = (x >> 16).astype(np.uint16)
+        w = (w >> 16).astype(np.uint16)
+    ref = oracle.router(x, w, act, None)
+    assert np.any((ref != 0) & (np.abs(ref) < np.float32(2.0 ** -126))), "no subnormal logits in the case"
+    lg = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    assert dg.moe_router_logits(to_device(x, DEV), to_device(w, DEV), lg, None) == 0
+    torch.cuda.synchronize()
+    got = lg.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{np.count_nonzero(got != ref)} logits differ"
 
 DISPATCH = [
     # T,    K,  E,   distribution
