@@ -14,10 +14,12 @@
 // whole line per weight row per 64-k stage, through a ring of three stages (two in flight while
 // one is multiplied), and the MFMA operands are read from LDS.
 //
-// Workgroup: four waves, 64 output columns of one group (wave w: 16 of them), every row of the
-// group in chunks of 64.  Stage slot: the chunk's activation rows [64][128 B], then the weight
-// rows [R][128 B] (R = 128 for GEMM-1: gate rows of the 64 columns, then their up rows; 64 for
-// GEMM-2).  Chunk c of row r sits at chunk c ^ swz(r) (the swizzle of the tiled kernels), so the
+// Workgroup: four waves, every row of the group in chunks of 64, and 128 weight rows: for GEMM-1
+// the gate rows of 64 output columns, then their up rows; for GEMM-2 128 output columns, as two
+// halves of 64 (wave w: columns [16 w, 16 w + 16) of each; 128 rather than 64 columns per
+// workgroup measured 607 -> 598 us for the DeepSeek-V3 decode batch).  Stage slot: the chunk's
+// activation rows [64][128 B], then the weight rows [128][128 B].  Chunk c of row r sits at
+// chunk c ^ swz(r) (the swizzle of the tiled kernels), so the
 // 16 rows of an MFMA operand read fall in distinct banks.  Weight DMA: instruction t of wave w
 // fetches rows [8 (w T + t), +8), lane i row + i / 8, the logical chunk its LDS slot holds.
 // Activation DMA: as in experts.hip, wave w copies rows [16 w, 16 w + 16) when the chunk has a
@@ -33,7 +35,7 @@ constexpr int SD_NS = 3;      // ring depth
 constexpr int SD_ROWB = 128;  // bytes per row and stage: 64 k of bf16
 constexpr int SD_AROWS = 64;  // activation rows per chunk
 constexpr int SD_A_BYTES = SD_AROWS * SD_ROWB;
-constexpr int sd_wrows(bool g1) { return g1 ? 128 : 64; }
+constexpr int sd_wrows(bool) { return 128; }
 constexpr int sd_stage_bytes(bool g1) { return SD_A_BYTES + sd_wrows(g1) * SD_ROWB; }
 constexpr int sd_lds_bytes(bool g1) { return SD_NS * sd_stage_bytes(g1); }
 
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(SD_THREADS) void stream_dma(GroupedArgs a, int32_t 
     constexpr int WR = sd_wrows(G1);
     constexpr int ST = sd_stage_bytes(G1);
     constexpr int WT = WR / 8 / 4;  // weight DMA instructions per wave per stage
-    constexpr int NW = G1 ? 2 : 1;  // weight matrices
+    constexpr int NW = 2;           // weight row blocks: gate and up (G1), or two 64-column halves
     const int32_t g = g0 + blockIdx.y;
     int32_t r0, cnt;
     if (g < a.E) {
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(SD_THREADS) void stream_dma(GroupedArgs a, int32_t 
     const bool shared = g == a.E;
     const int32_t N = G1 ? (shared ? a.Is : a.I) : a.H;
     const int32_t KD = G1 ? a.H : (shared ? a.Is : a.I);  // a multiple of 64
-    const int32_t col0 = blockIdx.x * 64;
+    const int32_t col0 = blockIdx.x * (G1 ? 64 : 128);
     if (col0 >= N) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int nst = KD >> 6;
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(SD_THREADS) void stream_dma(GroupedArgs a, int32_t 
     for (int t = 0; t < WT; ++t) {
         const int rho = (wave * WT + t) * 8 + (lane >> 3);  // slot row
         const int c = (lane & 7) ^ sd_swz(rho);
-        const int32_t n = col0 + (G1 ? (rho & 63) : rho);
+        const int32_t n = G1 ? col0 + (rho & 63) : min(col0 + rho, N - 1);  // rows past N: never stored
         w_off[t] = ((uint32_t)n * (uint32_t)KD + c * 8) * 2u;
     }
     const char* abase = G1 ? (const char*)a.x : (const char*)a.h;
@@ -187,10 +189,13 @@ __global__ __launch_bounds__(SD_THREADS) void stream_dma(GroupedArgs a, int32_t 
             for (int v = 0; v < 4; ++v) {
                 const int32_t rr = m0 + rb * 16 + q * 4 + v;
                 if (rr >= cnt) continue;
-                if (G1)
-                    ((bf16_t*)a.h)[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(sd_silu(acc[0][rb][v]) * acc[NW - 1][rb][v]);
-                else
-                    ((bf16_t*)a.o)[(int64_t)(r0 + rr) * a.H + col] = f32_to_bf16(acc[0][rb][v]);
+                if (G1) {
+                    ((bf16_t*)a.h)[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(sd_silu(acc[0][rb][v]) * acc[1][rb][v]);
+                } else {
+                    bf16_t* orow = (bf16_t*)a.o + (int64_t)(r0 + rr) * a.H;
+                    orow[col] = f32_to_bf16(acc[0][rb][v]);
+                    if (col + 64 < N) orow[col + 64] = f32_to_bf16(acc[1][rb][v]);
+                }
             }
         }
     }
@@ -219,7 +224,7 @@ hipError_t launch_stream_dma(const GroupedArgs& a, bool gemm1, int32_t g0, int32
         hipLaunchKernelGGL((stream_dma<true>), dim3((N + 63) / 64, g1 - g0), dim3(SD_THREADS), sd_lds_bytes(true), s, a,
                            g0);
     } else {
-        hipLaunchKernelGGL((stream_dma<false>), dim3((a.H + 63) / 64, g1 - g0), dim3(SD_THREADS), sd_lds_bytes(false),
+        hipLaunchKernelGGL((stream_dma<false>), dim3((a.H + 127) / 128, g1 - g0), dim3(SD_THREADS), sd_lds_bytes(false),
                            s, a, g0);
     }
     return hipGetLastError();
