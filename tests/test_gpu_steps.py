@@ -18,7 +18,7 @@ ROUTER_SHAPES = [
     (512, 1024, 64, "bf16"),
     (64, 7168, 256, "bf16"),
     (8192, 7168, 256, "bf16"),   # matrix-core kernel, DeepSeek-V3 prefill shape
-    (37, 200, 96, "f32"),        # ragged everywhere, partial k chunk
+    (37, 200, 96, "f32"),        # GEMV, rows not a multiple of 32 (the scalar-load kernel)
     (2049, 96, 1000, "bf16"),    # many experts, ragged token and expert tiles
     (1, 7168, 256, "bf16"),
     (2048, 7168, 256, "bf16"),
@@ -31,6 +31,7 @@ ROUTER_SHAPES = [
     (3000, 7168, 1, "bf16"),     # one expert (the shared-expert gate): GEMV at many tokens
     (37, 7168, 256, "bf16"),     # GEMV, ragged token block: row touching clamped to the block's rows
     (300, 520, 64, "bf16"),      # GEMV, short rows: every touching lane past a row's end clamped
+    (100, 16416, 32, "bf16"),    # GEMV with rows too long to stage in LDS (the scalar-load kernel)
 ]
 
 
