@@ -72,23 +72,28 @@ __device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_r
 
 struct TileArgs {
     GroupedArgs a;
-    const int32_t* tile_count;  // [1]
+    const int32_t* tile_count;  // [2]: tiles in the list, tiles of the groups below E (the routed
+                                //   ones; the shared expert's tiles follow them)
     const int32_t* tile_info;   // [max_tiles][4]: group, first row within the group, the group's
                                 //   first row in the row space, its row count
     int32_t g0, g1;             // groups handled by this launch
+    int32_t part;               // tiles it maps: 0 all, 1 those below E, 2 those from E on
     int32_t col_tiles;          // output column tiles per row tile
     int32_t nwg;                // workgroups launched
 };
 
-// Workgroup -> (tile, column tile).  The logical space holds tile_count * col_tiles items in
-// bands of CB column tiles (4 for the bf16 kernel, 2 for the quantised ones, measured): items of
-// one band walk the row tiles with the column fastest, so the
-// workgroups running at once share both A panels (same rows) and B panels (same group and
-// columns).  Workgroup ids congruent mod 8 land on the same XCD; each XCD takes one contiguous
-// eighth of the logical space, sized by the tile count actually built (the grid is a bound).
+// Workgroup -> (tile, column tile).  The logical space holds the launch's tiles (all of the
+// list, or only the routed or only the shared part of it, so that a launch over one part spreads
+// that part over every XCD) times col_tiles items, in bands of CB column tiles (4 for the bf16
+// kernel, 2 for the quantised ones, measured): items of one band walk the row tiles with the
+// column fastest, so the workgroups running at once share both A panels (same rows) and B panels
+// (same group and columns).  Workgroup ids congruent mod 8 land on the same XCD; each XCD takes
+// one contiguous eighth of the logical space, sized by the tile count actually built (the grid is
+// a bound).
 template <int32_t CB>
 __device__ __forceinline__ bool map_tile(const TileArgs& ta, int32_t& tile, int32_t& ct) {
-    const int32_t ntiles = ta.tile_count[0];
+    const int32_t t0 = ta.part == 2 ? ta.tile_count[1] : 0;
+    const int32_t ntiles = (ta.part == 1 ? ta.tile_count[1] : ta.tile_count[0]) - t0;
     const int32_t total = ntiles * ta.col_tiles;
     const int32_t per_xcd = (total + 7) / 8;
     const int32_t bid = blockIdx.x;
@@ -99,7 +104,7 @@ __device__ __forceinline__ bool map_tile(const TileArgs& ta, int32_t& tile, int3
     const int32_t band = l / (ntiles * CB);
     const int32_t bw = min(CB, ta.col_tiles - band * CB);
     const int32_t rem = l - band * ntiles * CB;
-    tile = rem / bw;
+    tile = t0 + rem / bw;
     ct = band * CB + rem % bw;
     return true;
 }
@@ -820,8 +825,10 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
         *(i32x4*)(tile_info + 4 * i) = i32x4{g, m * bm_of(g), r0, cnt};
     };
     for (int32_t m = 0; m < n; ++m) put(start + m, t, m);
+    if (t == E) tile_count[1] = start;  // the tiles of groups 0 .. E-1 come first
     if (t == 0) {
         int32_t total = buf[1023];
+        if (E >= 1024) tile_count[1] = total;
         if (ng > 1024) {
             const int32_t nn = ntiles(1024);
             for (int32_t m = 0; m < nn; ++m) put(total + m, 1024, m);
@@ -901,6 +908,7 @@ hipError_t launch_gemm_tiled(const GroupedArgs& a, bool gemm1, int32_t BM, int32
     ta.tile_info = tile_info;
     ta.g0 = g0;
     ta.g1 = g1;
+    ta.part = g0 >= a.E ? 2 : g1 <= a.E ? 1 : 0;
     const int32_t N = gemm1 ? (a.I > a.Is ? a.I : a.Is) : a.H;
     const int32_t out_cols = gemm1 ? NB / 2 : NB;
     ta.col_tiles = (N + out_cols - 1) / out_cols;
