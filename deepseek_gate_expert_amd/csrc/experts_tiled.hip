@@ -30,6 +30,7 @@ namespace {
 constexpr int NB = 256;       // weight rows per tile
 constexpr int THREADS = 256;  // 4 waves
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 
@@ -166,11 +167,11 @@ __device__ __forceinline__ void wait_stages(int later) {
 // left the k loop): each wave writes its bf16 results -- GEMM-1: bf16(silu(gate) * up), gate
 // accumulators in j = 0 and up in j = 1, 32 output columns per wave; GEMM-2: 64 columns -- into
 // a row-major image of the output tile, then all threads copy it out in 16-byte row pieces.
-// Written straight from the MFMA layout, every lane would store one column: 2-byte stores, 128
-// per lane for GEMM-2, which cost more than a tenth of the tile's time at K = 2048.  In the image
-// the 16-byte chunk c of row r sits at chunk c ^ (4 (r / 4 mod 2)), so the two rows one
-// ds_write_b16 touches (r and r + 4) fall in different banks.  Rows past the group and columns
-// past N are not stored.
+// The k loop multiplies with the weights as the MFMA's first operand, so a lane's accumulator
+// elements 4q .. 4q+3 are four consecutive output columns of one token row: each goes to the
+// image as one 8-byte write (16 per lane for GEMM-2 where 2-byte writes took 128).  In the image
+// the 16-byte chunk c of row r sits at chunk c ^ (r mod CPR), so the 32 rows of one write
+// instruction spread over every bank.  Rows past the group and columns past N are not stored.
 template <int BM, bool SWIGLU>
 __device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16 (&acc)[BM / 64][2], char* smem,
                                               int32_t r0, int32_t cnt, int32_t m0, int32_t n0, int32_t N, int wm,
@@ -181,21 +182,26 @@ __device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16
     constexpr int RB = OUT_COLS * 2;  // bytes per image row
     constexpr int CPR = OUT_COLS / 8;  // 16-byte chunks per row
     static_assert(BM * RB <= dma::ring_bytes(BM), "output image exceeds the ring");
-    const int lane = tid & 63, col_l = lane & 31, rsub = 4 * (lane >> 5);
-    auto cswz = [](int r) { return ((r >> 2) & 1) << 2; };
+    static_assert((CPR & (CPR - 1)) == 0, "chunks per row: a power of two");
+    const int lane = tid & 63, trow = lane & 31, half = lane >> 5;
+    auto chunk_at = [](int r, int c) { return r * RB + ((c ^ (r & (CPR - 1))) << 4); };
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave is done with the ring
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+        const int row = wm * WM + i * 32 + trow;
 #pragma unroll
         for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
-            const int col = SWIGLU ? wn * 32 + col_l : wn * 64 + j * 32 + col_l;
+            const int c0 = SWIGLU ? wn * 4 : wn * 8 + j * 4;  // first 16-byte chunk of the 32 columns
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = wm * WM + i * 32 + 8 * (v >> 2) + rsub + (v & 3);
-                const float val = SWIGLU ? silu_f(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
-                *(bf16_t*)(smem + row * RB + ((((col >> 3) ^ cswz(row)) << 4) | ((col & 7) << 1))) = f32_to_bf16(val);
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = SWIGLU ? silu_f(acc[i][0][4 * q + e]) * acc[i][1][4 * q + e] : acc[i][j][4 * q + e];
+                *(u32x2*)(smem + chunk_at(row, c0 + q) + half * 8) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             }
         }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     bf16_t* dst = SWIGLU ? (bf16_t*)a.h : (bf16_t*)a.o;
     const int64_t ld = SWIGLU ? a.ldh : a.H;
@@ -205,7 +211,7 @@ __device__ __forceinline__ void tile_epilogue(const GroupedArgs& a, const f32x16
         const int row = q / CPR, c = q % CPR;
         const int32_t col = n0 + c * 8;
         if (m0 + row >= cnt || col >= N) continue;
-        const u32x4 v = *(const u32x4*)(smem + row * RB + ((c ^ cswz(row)) << 4));
+        const u32x4 v = *(const u32x4*)(smem + chunk_at(row, c));
         *(u32x4*)(dst + (int64_t)(r0 + m0 + row) * ld + col) = v;
     }
 }
@@ -354,14 +360,14 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
         // issuing all reads after the first MFMA)
         auto mfma_step = [&](int buf, bool then_read, int rkt, int rs, int rbuf) {
             if constexpr (NV > 0) {
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][0], fb[buf][0], acc[0][0], 0, 0, 0);
+                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][0], fa[buf][0], acc[0][0], 0, 0, 0);
                 if (then_read) read_frags(rkt, rs, rbuf);
 #pragma unroll
                 for (int i = 0; i < NV; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
                         if (i | j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
                 // one MFMA, then one LDS read of the next step, alternating until the reads run out
 #pragma unroll
                 for (int q = 0; q < 2 * NV; ++q) {
@@ -675,7 +681,7 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
         for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < 2 * MT; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -728,30 +734,35 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
 
     // Epilogue through an LDS image of the output tile, as in gemm_dma: each lane writes its bf16
     // results -- GEMM-1: bf16(silu(gate) * up), 32 output columns per wave; GEMM-2: 64 -- into a
-    // row-major image (chunk c of row r at c ^ (4 (r / 4 mod 2)), so the two rows one
-    // ds_write_b16 covers fall in different banks), then every thread copies 16-byte row pieces
-    // out.  The ring is reused for the image once every wave's DMAs have landed (the loop's tail
-    // repeats the last stage's DMA) and every wave is past its last LDS read.
+    // row-major image, four consecutive columns of one row per 8-byte write (the weights are the
+    // MFMA's first operand), chunk c of row r at c ^ (r mod OCPR); then every thread copies
+    // 16-byte row pieces out.  The ring is reused for the image once every wave's DMAs have
+    // landed (the loop's tail repeats the last stage's DMA) and every wave is past its last LDS
+    // read.
     constexpr int OUT_COLS = SWIGLU ? NB / 2 : NB;
     constexpr int RB = OUT_COLS * 2;   // bytes per image row
     constexpr int OCPR = OUT_COLS / 8;  // 16-byte chunks per image row
     constexpr int NT = 256;             // threads of the workgroup
     static_assert(MT * 32 * RB <= wq::lds_bytes(WQ, SWIGLU, SIDE8), "output image exceeds the LDS allocation");
-    auto cswz = [](int r) { return ((r >> 2) & 1) << 2; };
+    static_assert((OCPR & (OCPR - 1)) == 0, "chunks per row: a power of two");
+    auto chunk_at = [](int r, int c) { return r * RB + ((c ^ (r & (OCPR - 1))) << 4); };
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int rgrp = (lane >> 5) * 4;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+        const int row = i * 32 + (lane & 31);
 #pragma unroll
         for (int j = 0; j < (SWIGLU ? 1 : 2); ++j) {
-            const int col = SWIGLU ? wave * 32 + (lane & 31) : wave * 64 + j * 32 + (lane & 31);
+            const int c0 = SWIGLU ? wave * 4 : wave * 8 + j * 4;  // first 16-byte chunk of the 32 columns
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = i * 32 + (v >> 2) * 8 + rgrp + (v & 3);
-                const float val = SWIGLU ? silu_f(acc[i][0][v]) * acc[i][1][v] : acc[i][j][v];
-                *(bf16_t*)(smem + row * RB + ((((col >> 3) ^ cswz(row)) << 4) | ((col & 7) << 1))) = f32_to_bf16(val);
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = SWIGLU ? silu_f(acc[i][0][4 * q + e]) * acc[i][1][4 * q + e] : acc[i][j][4 * q + e];
+                *(u32x2*)(smem + chunk_at(row, c0 + q) + half * 8) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             }
         }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     bf16_t* dst = SWIGLU ? (bf16_t*)a.h : (bf16_t*)a.o;
     const int64_t ld = SWIGLU ? a.ldh : a.H;
@@ -762,7 +773,7 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
         const int row = q / OCPR, c = q % OCPR;
         const int32_t col = n0 + c * 8;
         if (row >= rows || col >= N) continue;
-        const u32x4 v = *(const u32x4*)(smem + row * RB + ((c ^ cswz(row)) << 4));
+        const u32x4 v = *(const u32x4*)(smem + chunk_at(row, c));
         *(u32x4*)(dst + (int64_t)(r0 + m0 + row) * ld + col) = v;
     }
 }
