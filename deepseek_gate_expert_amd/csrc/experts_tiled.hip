@@ -584,18 +584,25 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
         nq = srow * (KD / 64);
     }
 
+    // Each DMA source is a uniform base (advanced by the stage) plus the lane's 32-bit offset.  The
+    // offsets pass through an empty asm (which the compiler must assume changes them) first:
+    // otherwise it hoists base + offset out of the loop as per-lane 64-bit pointers and adds the
+    // stage's advance to each with a 64-bit vector add on every stage.
     auto issue = [&](int kt) {
         char* st = smem + (kt % NS) * STAGE;
         const char* ab = (const char*)(a_base + kt * BKD);
 #pragma unroll
-        for (int j = 0; j < A_DMA; ++j)
-            __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[j]),
-                                             DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024), 16, 0, 0);
+        for (int j = 0; j < A_DMA; ++j) {
+            asm volatile("" : "+v"(a_off[j]));
+            __builtin_amdgcn_global_load_lds((const void*)(ab + a_off[j]), DSMOE_LDS_PTR(st + (wave * A_DMA + j) * 1024),
+                                             16, 0, 0);
+        }
         char* cst = st + A_BYTES + wave * 64 * F::CB;
 #pragma unroll
         for (int t = 0; t < F::C_DMA; ++t) {
             const int jj = ((t * F::ROWS_PER_DMA) >> 5) & 1;  // block of this instruction's rows
-            __builtin_amdgcn_global_load_lds((const void*)(c_base[jj] + c_off[t] + kt * F::CB),
+            asm volatile("" : "+v"(c_off[t]));
+            __builtin_amdgcn_global_load_lds((const void*)(c_base[jj] + kt * F::CB + c_off[t]),
                                              DSMOE_LDS_PTR(cst + t * 1024), 16, 0, 0);
         }
         char* sst = st + A_BYTES + F::C_BYTES + wave * 256;
