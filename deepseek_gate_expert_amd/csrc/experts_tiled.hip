@@ -729,7 +729,18 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
     wait_vm_barrier<(NS - 1) * D>();
     read_b(0, bs);
     frags(0, 0, 0, bs);
-    for (int kt = 0; kt < nk; ++kt) stage(kt);
+    // 4-bit: stages in pairs, so each one's ring slot (kt % NS, NS = 2) is known when it is
+    // compiled and its LDS addresses fold into the instructions' immediate offsets (measured about
+    // 1 % faster for 4-bit, no faster for fp8)
+    static_assert(NS == 2, "stage pairs assume a two-slot ring");
+    int kt = 0;
+    if constexpr (WQ == WQ_Q4) {
+        for (; kt + 2 <= nk; kt += 2) {
+            stage(kt);
+            stage(kt + 1);
+        }
+    }
+    for (; kt < nk; ++kt) stage(kt);
 
     // the accumulators of the last MFMAs are read right away: give the MFMA-to-VALU wait states
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
