@@ -442,12 +442,14 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 enum { WQ_Q4 = 0, WQ_F8 = 1 };
 
 namespace wq {
-// rows of the tile list's tiles: 128 for both formats, so two workgroups (64 KB of LDS and two
-// waves per SIMD between them) share a CU and one's dequantisation runs under the other's
-// MFMAs.  (256-row 4-bit tiles -- one workgroup per CU, each weight dequantised once per 256
-// rows -- measured about 2 % slower on the DeepSeek-V3 4-bit prefill layer, T = 4096, whose
-// groups average about 150 rows.)
-constexpr int bm(int) { return 128; }
+// rows of the tile list's tiles: 160 for 4-bit, 128 for fp8, so two workgroups (at most 80 KB of
+// LDS and two waves per SIMD each) share a CU and one's dequantisation runs under the other's
+// MFMAs.  A tile dequantises all of its 256 weight rows whatever its height, so the tallest tile
+// whose accumulators still fit two waves per SIMD (160 rows: 160 of a wave's 256 registers)
+// takes a group of 129..160 rows in one tile instead of two: 4.49 -> 4.39 ms on the DeepSeek-V3
+// 4-bit prefill layer (T = 4096, groups of about 150 rows).  (256-row 4-bit tiles -- one
+// workgroup per CU -- measured about 2 % slower than 128-row ones.)
+constexpr int bm(int wqt) { return wqt == WQ_Q4 ? 160 : 128; }
 template <int WQ>
 struct Fmt {
     static constexpr int BM = bm(WQ);
@@ -729,18 +731,7 @@ __device__ __forceinline__ void wq_tile(const TileArgs& ta, char* smem, int32_t 
     wait_vm_barrier<(NS - 1) * D>();
     read_b(0, bs);
     frags(0, 0, 0, bs);
-    // 4-bit: stages in pairs, so each one's ring slot (kt % NS, NS = 2) is known when it is
-    // compiled and its LDS addresses fold into the instructions' immediate offsets (measured about
-    // 1 % faster for 4-bit, no faster for fp8)
-    static_assert(NS == 2, "stage pairs assume a two-slot ring");
-    int kt = 0;
-    if constexpr (WQ == WQ_Q4) {
-        for (; kt + 2 <= nk; kt += 2) {
-            stage(kt);
-            stage(kt + 1);
-        }
-    }
-    for (; kt < nk; ++kt) stage(kt);
+    for (int kt = 0; kt < nk; ++kt) stage(kt);
 
     // the accumulators of the last MFMAs are read right away: give the MFMA-to-VALU wait states
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
@@ -813,7 +804,13 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     constexpr int BM = wq::bm(WQ);
     const int32_t rows = min(cnt - m0, (int32_t)BM);
     const int32_t q32 = __builtin_amdgcn_readfirstlane((rows + 31) >> 5);
-    static_assert(BM == 128, "tile height");
+    static_assert(BM == 128 || BM == 160, "tile height");
+    if constexpr (BM >= 160) {
+        if (q32 >= 5) {
+            wq_tile<WQ, SWIGLU, SIDE8, 5>(ta, smem, g, m0, r0, cnt, n0);
+            return;
+        }
+    }
     if (q32 >= 4) wq_tile<WQ, SWIGLU, SIDE8, 4>(ta, smem, g, m0, r0, cnt, n0);
     else if (q32 == 3) wq_tile<WQ, SWIGLU, SIDE8, 3>(ta, smem, g, m0, r0, cnt, n0);
     else if (q32 == 2) wq_tile<WQ, SWIGLU, SIDE8, 2>(ta, smem, g, m0, r0, cnt, n0);
