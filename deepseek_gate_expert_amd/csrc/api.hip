@@ -53,8 +53,8 @@ struct TilePlan {
 };
 
 // Shapes-only decision (no device reads).  bf16 weights: tiles of 256 rows when the average
-// group is large, else 128.  4-bit and fp8 weights: the height of their kernel (128 rows), each
-// tile computed at its real height rounded up to 32 rows.
+// group is large, else 128.  4-bit and fp8 weights: the height of their kernel (160 and 128
+// rows), each tile computed at its real height rounded up to 32 rows.
 TilePlan plan_tiles(const moe_layer_desc* d, bool allow256) {
     TilePlan p{false, 128, 128, 0, STREAM_MAX_ROWS};
     if (d->act_dtype != MOE_BF16 || d->T <= STREAM_MAX_ROWS) return p;

@@ -412,8 +412,8 @@ __global__ __launch_bounds__(dma::THREADS) void gemm_dma(TileArgs ta) {
 
 // ---------------------------------------------------------------------------------------------
 // Quantised weights: 4-bit (affine, groups of 64 along the reduction axis) or fp8 (OCP E4M3
-// codes, one fp32 scale per 128 x 128 block), tiles of 128 rows x 256 weight rows, same tile list
-// as gemm_dma.  A tile computes only its real rows rounded up to
+// codes, one fp32 scale per 128 x 128 block), tiles of 160 (4-bit) or 128 (fp8) rows x 256
+// weight rows, same tile list as gemm_dma.  A tile computes only its real rows rounded up to
 // 32 (a variant per height), while its weights are staged and dequantised once whatever its
 // height.  Every operand of a 64-k stage -- the activation rows, the weight codes and the
 // scales (and 4-bit offsets) -- enters LDS by DMA, in a ring of two stages (stage kt+1 in flight

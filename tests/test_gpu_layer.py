@@ -44,8 +44,9 @@ def tile_rows(oi, K, BM=128):
     """Tokens that put a row into every BM-row tile of every expert group, in the layout the
     dispatch gives a group (its slots in ascending order): the first row of each group and the
     last row of each of its tiles (so every ragged last tile too).  128-row tiles cover the
-    256-row tiles of the bf16 kernel twice and the quantised kernels' 128-row tiles once; a group
-    of at most 64 rows (streamed in bf16 layers) is one tile."""
+    256-row tiles of the bf16 kernel twice, the 4-bit kernel's 160-row tiles and the fp8 kernel's
+    128-row tiles at least once (every span of 128 or more rows holds the end of a 128-row block);
+    a group of at most 64 rows (streamed in bf16 layers) is one tile."""
     flat = oi.ravel()
     rows = set()
     for e in np.unique(flat):
@@ -266,7 +267,8 @@ def test_layer_fp8_every_code(T):
 # Group sizes chosen to meet every tile-height variant: the last tile of a group holds 1..BM rows,
 # which selects how many 32-row blocks each wave of the bf16 kernel multiplies (0..4 per half of a
 # 256-row tile, 0..2 per half of a 128-row one) and which height variant of the quantised kernels
-# runs (1..4 blocks of 32 rows of their 128-row tiles); groups of at most 64 rows are streamed in
+# runs (1..5 blocks of 32 rows of the 4-bit kernel's 160-row tiles, 1..4 of the fp8 kernel's
+# 128-row ones); groups of at most 64 rows are streamed in
 # bf16 layers and tiled in quantised ones; two experts receive no rows.  SIZES_256 has a mean
 # group (over all 18 experts) of 192 rows, so bf16 layers use 256-row tiles; SIZES_128 a mean of
 # 133 (128-row tiles).
