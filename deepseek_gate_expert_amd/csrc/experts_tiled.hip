@@ -821,8 +821,10 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
 // Tile list (offsets is read only for routed groups: it may be NULL when E == 0): every group in
 // [0, E] (E = shared expert) with more than `min_rows` rows gets
 // ceil(rows / BM) tiles (ceil(T / BMs) for the shared expert, whose tiles a launch of their own
-// may compute with a different tile height), in group order.  One workgroup; group 1024 (only
-// possible with E == 1024 plus a shared expert) is appended by thread 0.
+// may compute with a different tile height), in group order; tile_count[0] is the number of
+// tiles, tile_count[1] the number of routed ones (those before the shared expert's).  One
+// workgroup; group 1024 (only possible with E == 1024 plus a shared expert) is appended by
+// thread 0.
 __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ offsets, int32_t E, int64_t T,
                                                      int32_t TK, int32_t has_shared, int32_t BM, int32_t BMs,
                                                      int32_t min_rows,
