@@ -33,9 +33,10 @@ METRIC = "MoE-layer tokens/sec (DeepSeek-V3 shape, bf16) + % HBM/MFMA peak"
 # summary under profiles/ (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, over this script, each
 # scaled by what the same counter reads for the plain 256 MiB device copy that main() runs
 # first).  FETCH_SIZE counts the L2's reads from the memory side, so it includes reads that the
-# memory-attached last-level cache serves.  The summary records the sha256 of the kernel's
-# source file when the counters were taken; if that file has changed since, the figure no longer
-# describes the kernel and "traffic" is null.
+# memory-attached last-level cache serves.  The summary records a sha256 of the kernel's source
+# file, taken over its code with comments removed and whitespace collapsed, when the counters were
+# taken; if that code has changed since, the figure no longer describes the kernel and "traffic"
+# is null (a change to comments alone keeps it).
 TRAFFIC_PROFILES = {
     "c3": ("gemm_dma_gate_up_dsv3_prefill_T8192_hbm_traffic.md", "experts_tiled.hip"),
     "c2": ("stream_dma_gate_up_dsv3_decode_T64_hbm_traffic.md", "experts_stream.hip"),
@@ -43,9 +44,34 @@ TRAFFIC_PROFILES = {
 }
 
 
+def code_sha256(path: str) -> str:
+    """sha256 of a C/HIP source's code: comments removed, whitespace runs collapsed to one space."""
+    import hashlib
+    src = open(path).read()
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return hashlib.sha256(" ".join("".join(out).split()).encode()).hexdigest()
+
+
 def traffic_gb(workload: str):
     """(GB per launch, summary file) from the committed summary, or (None, reason)."""
-    import hashlib
     import re
     if workload not in TRAFFIC_PROFILES:
         return None, "no counter summary for this workload"
@@ -56,11 +82,10 @@ def traffic_gb(workload: str):
     except OSError:
         return None, f"profiles/{prof} missing"
     m_gb = re.search(r"^traffic_gb_per_launch:\s*([0-9.]+)\s*$", text, re.M)
-    m_sha = re.search(r"^source_sha256:\s*(\S+)\s+(\S+)\s*$", text, re.M)
+    m_sha = re.search(r"^code_sha256:\s*(\S+)\s+(\S+)\s*$", text, re.M)
     if not (m_gb and m_sha) or m_sha.group(1) != src:
         return None, f"profiles/{prof} has no machine-readable figure"
-    cur = hashlib.sha256(open(os.path.join(ROOT, "deepseek_gate_expert_amd", "csrc", src), "rb").read()).hexdigest()
-    if cur != m_sha.group(2):
+    if code_sha256(os.path.join(ROOT, "deepseek_gate_expert_amd", "csrc", src)) != m_sha.group(2):
         return None, f"{src} changed since the counters in profiles/{prof} were taken"
     return float(m_gb.group(1)), f"profiles/{prof}"
 
