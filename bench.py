@@ -380,6 +380,9 @@ def main():
                     "traffic_source": tr_src,
                     "kernel": ("stream_dma<gate/up> (bf16 weights streamed through an LDS DMA ring, gate/up + SwiGLU)"
                                if wl.expert == "bf16" else
+                               "stream_f8<gate/up> (fp8 codes of groups of <= 32 rows streamed through an LDS DMA "
+                               "ring, the bf16 shared expert through registers, gate/up + SwiGLU)"
+                               if wl.expert == "fp8" else
                                f"stream_gemm<{wl.expert}, gate/up> (weight-streaming gate/up + SwiGLU)")}
             layer = layer_bytes(wl, res["n_hit"]) / (res["step_ms"] / 1e3) / 1e9
             roof["layer_achieved"] = layer

@@ -151,6 +151,7 @@ inline int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 constexpr int MAX_DEVICES = 64;
 int g_tiled_state[MAX_DEVICES];
 bool g_stream_dma_ok[MAX_DEVICES];  // the DMA weight-streaming kernels may take their LDS
+bool g_stream_f8_ok[MAX_DEVICES];   // likewise the fp8 ones
 std::once_flag g_tiled_once[MAX_DEVICES];
 
 int tiled_state() {
@@ -165,6 +166,7 @@ int tiled_state() {
             else if (lds >= tiled_lds_bytes(128)) st = 2;
         }
         g_stream_dma_ok[dev] = configure_stream_dma() == hipSuccess;
+        g_stream_f8_ok[dev] = configure_stream_f8() == hipSuccess;
         (void)hipGetLastError();
         g_tiled_state[dev] = st;
     });
@@ -178,6 +180,15 @@ bool use_stream_dma(const GroupedArgs& a) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return false;
     tiled_state();
     return g_stream_dma_ok[dev] && stream_dma_fits(a);
+}
+
+// fp8 codes of small groups through the LDS DMA ring when the device allows its LDS and the
+// reduction lengths suit it; else the register-streaming kernel for every group
+bool use_stream_f8(const GroupedArgs& a) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return false;
+    tiled_state();
+    return g_stream_f8_ok[dev] && stream_f8_fits(a);
 }
 
 // Dense SwiGLU MLP: the shared-expert path on its own (group E with E = 0 routed experts).
@@ -341,6 +352,7 @@ int launch_forward(const moe_layer_desc* d, const void* x, const void* router_w,
         if (f32) return hip_rc(first ? launch_gemm1_f32(a, s) : launch_gemm2_f32(a, s));
         if (tp.on && tp.min_rows == 0) return MOE_OK;  // every group is tiled
         if (!quant && use_stream_dma(a)) return hip_rc(launch_stream_dma(a, first, 0, gend, s));
+        if (rdt == MOE_FP8 && use_stream_f8(a)) return hip_rc(launch_stream_f8(a, first, 0, gend, s));
         return hip_rc(first ? launch_gemm1_bf16(a, 0, gend, rdt, s) : launch_gemm2_bf16(a, 0, gend, rdt, s));
     };
     // tiled kernels of one pass (the other groups)

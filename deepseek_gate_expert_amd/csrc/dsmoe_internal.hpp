@@ -97,6 +97,11 @@ hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32
 hipError_t configure_stream_dma();
 bool stream_dma_fits(const GroupedArgs& a);
 hipError_t launch_stream_dma(const GroupedArgs& a, bool gemm1, int32_t g0, int32_t g1, hipStream_t s);
+// fp8 layers: routed groups of at most 32 rows stream their codes through an LDS DMA ring, the
+// rest as launch_gemm1_bf16 / launch_gemm2_bf16 would; configure once per device
+hipError_t configure_stream_f8();
+bool stream_f8_fits(const GroupedArgs& a);
+hipError_t launch_stream_f8(const GroupedArgs& a, bool gemm1, int32_t g0, int32_t g1, hipStream_t s);
 // fp32 layers: all routed rows and the shared rows in one launch each
 hipError_t launch_gemm1_f32(const GroupedArgs& a, hipStream_t s);
 hipError_t launch_gemm2_f32(const GroupedArgs& a, hipStream_t s);

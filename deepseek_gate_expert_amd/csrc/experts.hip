@@ -211,20 +211,20 @@ template <int N>
 __device__ __forceinline__ void s_wait_barrier() { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory"); }
 
 // GEMM-1 (G1): h = SwiGLU of x rows against W_gate / W_up;  GEMM-2: o = h rows against W_down.
-// One workgroup's share of group g: 64 output columns (blockIdx.x), every row of the group.
+// One workgroup's share of group g: 64 output columns (column block cb), every row of the group.
 // N is a multiple of 64 (bf16, 4-bit and fp8 layers), so every wave of a live workgroup has
 // columns.  As: the activation ring (three buffers, two steps ahead).
 template <int WF, bool G1>
-__device__ __forceinline__ void stream_body(const GroupedArgs& a, int32_t g, char* As) {
+__device__ __forceinline__ void stream_body(const GroupedArgs& a, int32_t g, int32_t cb, char* As) {
     int32_t r0, cnt;
     group_rows(a, g, r0, cnt);
     if (cnt <= 0 || cnt > a.stream_max_rows) return;
     const bool shared = g == a.E;
     const int32_t N = G1 ? (shared ? a.Is : a.I) : a.H;   // output columns
     const int32_t KD = G1 ? a.H : (shared ? a.Is : a.I);  // reduction length, a multiple of 64
-    if ((int32_t)blockIdx.x * 64 >= N) return;            // workgroup-uniform
+    if (cb * 64 >= N) return;                             // workgroup-uniform
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int32_t col = blockIdx.x * 64 + wave * 16 + (lane & 15);
+    const int32_t col = cb * 64 + wave * 16 + (lane & 15);
     const WRow w0 = weight_row<WF>(a, G1 ? 0 : 2, g, shared, col, N, KD);
     const WRow w1 = G1 ? weight_row<WF>(a, 1, g, shared, col, N, KD) : w0;
     const bf16_t* abase = G1 ? (const bf16_t*)a.x : (const bf16_t*)a.h;
@@ -390,9 +390,206 @@ __global__ __launch_bounds__(256) void stream_gemm(GroupedArgs a, int32_t g0) {
     __shared__ __attribute__((aligned(1024))) char As[3 * S_TILE];
     const int32_t g = g0 + blockIdx.y;
     if (WF != WF_BF16 && g == a.E)  // workgroup-uniform
-        stream_body<WF_BF16, G1>(a, g, As);
+        stream_body<WF_BF16, G1>(a, g, blockIdx.x, As);
     else
-        stream_body<WF, G1>(a, g, As);
+        stream_body<WF, G1>(a, g, blockIdx.x, As);
+}
+
+// ---- fp8 groups of at most 32 rows: codes through an LDS DMA ring ----
+//
+// Register loads in the MFMA operand layout cover half of a 128-byte line per weight row per
+// instruction and top out near 6.1 TB/s.  LDS DMA instructions in which eight lanes fetch one
+// whole line reach about 7.1 TB/s on the streaming pattern below (128 code rows per workgroup,
+// one line of each per stage, two stages in flight, two workgroups per CU), and still about
+// 6.9 TB/s with an fp8 stage's dequantisation and MFMAs between the waits; with one workgroup
+// per CU the same work drops to about 5 TB/s (measured on MI355X).  So the codes of fp8 groups
+// of up to 32 rows (the decode regime) stream this way.  Per 128-k stage a workgroup receives
+// one line of each of its 128 code rows -- GEMM-1: the gate rows of its 64 output columns,
+// then their up rows; GEMM-2: 128 output columns as two halves of 64 -- beside 256 bytes of
+// each of the chunk's 32 activation rows, in a ring of three 24 KB stages (72 KB: two
+// workgroups per CU).  The workgroup's output columns lie in one 128-row scale block, so each
+// stage needs one fp32 block scale per weight matrix; the block-scale rows (at most 64 stages)
+// are copied into LDS once by wave 0 before the first stage and read there by broadcast.
+// Slots: code chunk c (16 codes) of slot row rho sits at chunk c ^ f8d_swz(rho) and activation
+// chunk c (8 k) of row r at chunk c ^ (r mod 16), so the 8-byte code reads and 16-byte
+// activation reads of a 16-row MFMA operand fall in distinct banks.
+constexpr int F8D_NS = 3;                                   // ring depth
+constexpr int F8D_WROWS = 128;                              // code rows per stage
+constexpr int F8D_AROWS = 32;                               // activation rows (the largest group)
+constexpr int F8D_A_BYTES = F8D_AROWS * 256;                // 128 k of bf16 per activation row
+constexpr int F8D_STAGE = F8D_A_BYTES + F8D_WROWS * 128;    // 24 KB
+constexpr int F8D_SCALES = 2 * 256;                         // 64 fp32 scales per weight matrix
+constexpr int F8D_LDS = F8D_NS * F8D_STAGE + F8D_SCALES;
+constexpr int F8D_MAX_STAGES = 64;
+
+__device__ __forceinline__ int f8d_swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int N>
+__device__ __forceinline__ void f8d_wait_barrier() { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory"); }
+
+// group g (rows [r0, r0 + cnt), 1 <= cnt <= 32, fp8 codes), the workgroup's column block
+// blockIdx.x: 64 output columns for GEMM-1, 128 for GEMM-2.  The reduction length is a multiple
+// of 128 of at most 64 stages (checked by the launcher).
+template <bool G1>
+__device__ __forceinline__ void stream_f8_dma_body(const GroupedArgs& a, int32_t g, int32_t r0, int32_t cnt,
+                                                   char* smem) {
+    const int32_t N = G1 ? a.I : a.H;
+    const int32_t KD = G1 ? a.H : a.I;
+    const int32_t col0 = (int32_t)blockIdx.x * (G1 ? 64 : 128);
+    if (col0 >= N) return;  // workgroup-uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int nst = KD >> 7;
+    constexpr int WT = F8D_WROWS / 8 / 4;  // code DMA instructions per wave per stage
+    constexpr int NW = 2;                  // weight row blocks: gate and up, or two halves of 64 columns
+
+    // code rows: uniform expert bases plus per-lane 32-bit byte offsets (N * KD < 2^32)
+    const int64_t ebase = (int64_t)g * N * KD;
+    const char* wb0 = (const char*)(G1 ? a.wg : a.wd) + ebase;
+    const char* wb1 = (const char*)(G1 ? a.wu : a.wd) + ebase;
+    uint32_t w_off[WT];
+#pragma unroll
+    for (int t = 0; t < WT; ++t) {
+        const int rho = (wave * WT + t) * 8 + (lane >> 3);  // slot row
+        const int c = (lane & 7) ^ f8d_swz(rho);
+        const int32_t n = G1 ? col0 + (rho & 63) : min(col0 + rho, N - 1);  // rows past N: never stored
+        w_off[t] = (uint32_t)n * (uint32_t)KD + (uint32_t)c * 16u;
+    }
+    // block-scale rows of the workgroup's 128-row block: [E][ceil(N / 128)][nst] per matrix
+    const int64_t srow = ((int64_t)g * ((N + 127) >> 7) + (col0 >> 7)) * nst;
+    const float* fs0 = (G1 ? a.fsg : a.fsd) + srow;
+    const float* fs1 = (G1 ? a.fsu : a.fsd) + srow;
+    char* scl = smem + F8D_NS * F8D_STAGE;
+
+    // activation rows: wave w (w < nrb) copies rows [16 w, 16 w + 16), instruction j rows
+    // 16 w + 4 j + lane / 16; lane i fills chunk slot i % 16 of its row
+    const int nrb = (cnt + 15) >> 4;     // live 16-row blocks (1 or 2)
+    const bool copier = wave < nrb;      // wave-uniform
+    const char* abase = G1 ? (const char*)a.x : (const char*)a.h;
+    const int64_t lda = G1 ? a.H : a.ldh;
+    const char* arow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = wave * 16 + j * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        int32_t rr = r < cnt ? r : cnt - 1;  // rows past the group are computed, never stored
+        const int64_t src = G1 ? (int64_t)row_token(a, r0 + rr) : (int64_t)(r0 + rr);
+        arow[j] = abase + (src * lda + c * 8) * 2;
+    }
+    auto issue = [&](int s) {
+        char* st = smem + (s % F8D_NS) * F8D_STAGE;
+        if (copier) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                __builtin_amdgcn_global_load_lds((const void*)(arow[j] + s * 256),
+                                                 DSMOE_S_LDS(st + (wave * 4 + j) * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < WT; ++t) {
+            const int rho0 = (wave * WT + t) * 8;
+            const char* wb = (G1 && rho0 >= 64) ? wb1 : wb0;
+            __builtin_amdgcn_global_load_lds((const void*)(wb + w_off[t] + s * 128),
+                                             DSMOE_S_LDS(st + F8D_A_BYTES + rho0 * 128), 16, 0, 2 /* non-temporal */);
+        }
+    };
+
+    f32x4 acc[NW][2];
+#pragma unroll
+    for (int m = 0; m < NW; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int q = lane >> 4, ln = lane & 15;
+    auto compute = [&](int s) {
+        const char* st = smem + (s % F8D_NS) * F8D_STAGE;
+        const float sc0 = *(const float*)(scl + s * 4), sc1 = *(const float*)(scl + 256 + s * 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {  // four 32-k steps per stage
+            const int p = t * 4 + q;   // the lane's 8-k piece of the stage
+            bf16x8 wf[NW];
+#pragma unroll
+            for (int m = 0; m < NW; ++m) {
+                const int rho = m * 64 + wave * 16 + ln;
+                const u32x2 cw = *(const u32x2*)(st + F8D_A_BYTES + rho * 128 + (((p >> 1) ^ f8d_swz(rho)) << 4) + (p & 1) * 8);
+                wf[m] = dequant_f8x8(cw[0], cw[1], (G1 && m) ? sc1 : sc0);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                if (rb >= nrb) break;
+                const bf16x8 af = as_bf16x8(*(const u32x4*)(st + (rb * 16 + ln) * 256 + ((p ^ ln) << 4)));
+#pragma unroll
+                for (int m = 0; m < NW; ++m)
+                    acc[m][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wf[m], acc[m][rb], 0, 0, 0);
+            }
+        }
+    };
+
+    // wave 0 (always a copier) copies the scale rows first; the first stage's wait covers them
+    if (wave == 0) {
+        const int i = min(lane, nst - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(fs0 + i), DSMOE_S_LDS(scl), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(fs1 + i), DSMOE_S_LDS(scl + 256), 4, 0, 0);
+    }
+    issue(0);
+    if (nst > 1) issue(1);
+    for (int s = 0; s < nst; ++s) {
+        // stage s has landed for every wave; stage s+1 (if issued) may still be in flight
+        if (s + 1 < nst) {
+            if (copier) f8d_wait_barrier<WT + 4>();  // wave-uniform; both arms hold one barrier
+            else f8d_wait_barrier<WT>();
+        } else {
+            f8d_wait_barrier<0>();
+        }
+        // the slot of stage s+2 held stage s-1, which every wave finished before this barrier
+        if (s + 2 < nst) issue(s + 2);
+        compute(s);
+    }
+    // the accumulators are read right after the last MFMAs, possibly behind the row-block
+    // branch: issue the MFMA-to-VALU wait states explicitly before any of them is read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
+#pragma unroll
+    for (int m = 0; m < NW; ++m)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+            if (m | rb) asm volatile("" : "+a"(acc[m][rb]));
+    const int32_t col = col0 + wave * 16 + ln;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        if (rb >= nrb) break;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int32_t rr = rb * 16 + q * 4 + v;
+            if (rr >= cnt) continue;
+            if (G1) {
+                ((bf16_t*)a.h)[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[0][rb][v]) * acc[1][rb][v]);
+            } else {
+                bf16_t* orow = (bf16_t*)a.o + (int64_t)(r0 + rr) * a.H;
+                orow[col] = f32_to_bf16(acc[0][rb][v]);
+                if (col + 64 < N) orow[col + 64] = f32_to_bf16(acc[1][rb][v]);
+            }
+        }
+    }
+}
+
+// fp8 layers' weight streaming: routed groups of at most 32 rows through the DMA ring above; the
+// shared expert (bf16) and fp8 groups of 33 or more rows by the register-streaming body, which
+// owns 64 output columns per call (a GEMM-2 workgroup here owns 128: two calls).
+// grid: x = ceil(N / 64) (GEMM-1, N = max(I, Is)) or ceil(H / 128) (GEMM-2) column blocks,
+// y = groups [g0, g0 + gridDim.y), the last group first: workgroups are dispatched in grid
+// order, and the last group -- the shared expert, whose workgroups move twice the bytes of a
+// routed fp8 one, through registers -- would otherwise run alone at the end of the launch.
+template <bool G1>
+__global__ __launch_bounds__(256) void stream_f8(GroupedArgs a, int32_t g0) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int32_t g = g0 + (int32_t)((blockIdx.y + gridDim.y - 1) % gridDim.y);
+    int32_t r0, cnt;
+    group_rows(a, g, r0, cnt);
+    if (cnt <= 0 || cnt > a.stream_max_rows) return;  // workgroup-uniform
+    if (g < a.E && cnt <= F8D_AROWS) {
+        stream_f8_dma_body<G1>(a, g, r0, cnt, smem);
+        return;
+    }
+    const int32_t cb = G1 ? (int32_t)blockIdx.x : 2 * (int32_t)blockIdx.x;
+    for (int h = 0; h < (G1 ? 1 : 2); ++h) {
+        if (g == a.E) stream_body<WF_BF16, G1>(a, g, cb + h, smem);
+        else stream_body<WF_F8, G1>(a, g, cb + h, smem);
+    }
 }
 
 }  // namespace
@@ -419,6 +616,28 @@ hipError_t launch_gemm2_bf16(const GroupedArgs& a, int32_t g0, int32_t g1, int32
         hipLaunchKernelGGL((stream_gemm<WF_Q4, false>), grid, dim3(256), 0, s, a, g0);
     else
         hipLaunchKernelGGL((stream_gemm<WF_BF16, false>), grid, dim3(256), 0, s, a, g0);
+    return hipGetLastError();
+}
+
+hipError_t configure_stream_f8() {
+    hipError_t e = hipFuncSetAttribute((const void*)stream_f8<true>, hipFuncAttributeMaxDynamicSharedMemorySize, F8D_LDS);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void*)stream_f8<false>, hipFuncAttributeMaxDynamicSharedMemorySize, F8D_LDS);
+}
+
+// the DMA ring takes reduction lengths that are multiples of 128 of at most 64 stages
+bool stream_f8_fits(const GroupedArgs& a) {
+    return a.H % 128 == 0 && a.I % 128 == 0 && a.H <= 128 * F8D_MAX_STAGES && a.I <= 128 * F8D_MAX_STAGES;
+}
+
+hipError_t launch_stream_f8(const GroupedArgs& a, bool gemm1, int32_t g0, int32_t g1, hipStream_t s) {
+    if (g1 <= g0) return hipSuccess;
+    if (gemm1) {
+        const int32_t N = max(a.I, a.Is);
+        hipLaunchKernelGGL((stream_f8<true>), dim3((N + 63) / 64, g1 - g0), dim3(256), F8D_LDS, s, a, g0);
+    } else {
+        hipLaunchKernelGGL((stream_f8<false>), dim3((a.H + 127) / 128, g1 - g0), dim3(256), F8D_LDS, s, a, g0);
+    }
     return hipGetLastError();
 }
 

@@ -276,6 +276,13 @@ SIZES_256 = [1, 33, 64, 65, 96, 0, 128, 129, 160, 161, 200, 0, 250, 256, 257, 30
 SIZES_128 = [1, 40, 64, 65, 80, 0, 96, 97, 127, 128, 129, 0, 150, 200, 255, 256, 300, 412]
 
 
+# Streamed layers (T <= 64): groups of 1..64 rows.  fp8 groups of at most 32 rows stream their
+# codes through the LDS DMA ring (one or two 16-row blocks), larger ones and the bf16 shared
+# expert through registers, in the same launch; H = 256 / I = 128 give one- and two-stage
+# reductions, H = 1024 / I = 512 several stages.
+SIZES_STREAM = [1, 15, 16, 17, 31, 32, 33, 0, 47, 64]
+
+
 def exact_group_case(sizes, K, expert, H=256, I=128):
     """A layer whose routing puts exactly sizes[e] rows in group e: the router is the identity on
     the first E input columns and token t carries 4.0 in the columns of its K experts (0 in the
@@ -299,8 +306,11 @@ def exact_group_case(sizes, K, expert, H=256, I=128):
 
 @pytest.mark.parametrize("sizes,expert,H,I", [(SIZES_256, "bf16", 256, 128), (SIZES_128, "bf16", 256, 128),
                                               (SIZES_256, "q4", 256, 128), (SIZES_256, "q4", 1024, 512),
-                                              (SIZES_128, "fp8", 256, 128), (SIZES_256, "fp8", 256, 128)],
-                         ids=["bf16_tiles256", "bf16_tiles128", "q4", "q4_side_chunks", "fp8", "fp8_tall_groups"])
+                                              (SIZES_128, "fp8", 256, 128), (SIZES_256, "fp8", 256, 128),
+                                              (SIZES_STREAM, "fp8", 256, 128), (SIZES_STREAM, "fp8", 1024, 512),
+                                              (SIZES_STREAM, "bf16", 1024, 512)],
+                         ids=["bf16_tiles256", "bf16_tiles128", "q4", "q4_side_chunks", "fp8", "fp8_tall_groups",
+                              "fp8_streamed", "fp8_streamed_long", "bf16_streamed"])
 def test_layer_exact_group_sizes(sizes, expert, H, I):
     w, r, b, x, ex, sh, off = exact_group_case(sizes, 4, expert, H, I)
     log(f"[groups] {expert}: T={w.T} sizes {sizes}")
