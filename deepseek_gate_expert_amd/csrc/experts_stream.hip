@@ -59,7 +59,9 @@ __global__ __launch_bounds__(SD_THREADS) void stream_dma(GroupedArgs a, int32_t 
     constexpr int ST = sd_stage_bytes(G1);
     constexpr int WT = WR / 8 / 4;  // weight DMA instructions per wave per stage
     constexpr int NW = 2;           // weight row blocks: gate and up (G1), or two 64-column halves
-    const int32_t g = g0 + blockIdx.y;
+    // the last group of the launch first: workgroups are dispatched in grid order, and the last
+    // group -- the shared expert, whose chunk holds every token -- would otherwise end the launch
+    const int32_t g = g0 + (int32_t)((blockIdx.y + gridDim.y - 1) % gridDim.y);
     int32_t r0, cnt;
     if (g < a.E) {
         r0 = a.offsets[g];
