@@ -427,18 +427,25 @@ __device__ __forceinline__ int f8d_swz(int r) { return (r ^ (r >> 3)) & 7; }
 template <int N>
 __device__ __forceinline__ void f8d_wait_barrier() { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory"); }
 
-// group g (rows [r0, r0 + cnt), 1 <= cnt <= 32, fp8 codes), the workgroup's column block
-// blockIdx.x: 64 output columns for GEMM-1, 128 for GEMM-2.  The reduction length is a multiple
-// of 128 of at most 64 stages (checked by the launcher).
+// group g (rows [r0, r0 + cnt), 1 <= cnt <= 32, fp8 codes), the workgroup's nbw column blocks
+// from nbw * blockIdx.x on: 64 output columns each for GEMM-1, 128 for GEMM-2.  The blocks'
+// stages form one stream through the ring (the next block's first stages load under the last
+// stages of the one before), so a short reduction does not refill the ring per block.  The
+// reduction length is a multiple of 128, and nbw times its stages at most 64 (checked by the
+// launcher).
 template <bool G1>
 __device__ __forceinline__ void stream_f8_dma_body(const GroupedArgs& a, int32_t g, int32_t r0, int32_t cnt,
-                                                   char* smem) {
+                                                   int32_t nbw, char* smem) {
     const int32_t N = G1 ? a.I : a.H;
     const int32_t KD = G1 ? a.H : a.I;
-    const int32_t col0 = (int32_t)blockIdx.x * (G1 ? 64 : 128);
+    constexpr int CW = G1 ? 64 : 128;  // output columns per block
+    const int32_t cb0 = (int32_t)blockIdx.x * nbw;
+    const int32_t col0 = cb0 * CW;
     if (col0 >= N) return;  // workgroup-uniform
+    const int nb = min(nbw, (N + CW - 1) / CW - cb0);  // live blocks
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int nst = KD >> 7;
+    const int ntot = nb * nst;  // stages of all blocks, at most 64
     constexpr int WT = F8D_WROWS / 8 / 4;  // code DMA instructions per wave per stage
     constexpr int NW = 2;                  // weight row blocks: gate and up, or two halves of 64 columns
 
@@ -446,15 +453,19 @@ __device__ __forceinline__ void stream_f8_dma_body(const GroupedArgs& a, int32_t
     const int64_t ebase = (int64_t)g * N * KD;
     const char* wb0 = (const char*)(G1 ? a.wg : a.wd) + ebase;
     const char* wb1 = (const char*)(G1 ? a.wu : a.wd) + ebase;
-    uint32_t w_off[WT];
+    // byte offset of each DMA instruction's source in the first block's code rows; a later GEMM-2
+    // block adds 128 rows, clamped to the last row (rows past N are never stored)
+    int w_rho[WT];
+    uint32_t w_c[WT], w_off[WT];
 #pragma unroll
     for (int t = 0; t < WT; ++t) {
-        const int rho = (wave * WT + t) * 8 + (lane >> 3);  // slot row
-        const int c = (lane & 7) ^ f8d_swz(rho);
-        const int32_t n = G1 ? col0 + (rho & 63) : min(col0 + rho, N - 1);  // rows past N: never stored
-        w_off[t] = (uint32_t)n * (uint32_t)KD + (uint32_t)c * 16u;
+        w_rho[t] = (wave * WT + t) * 8 + (lane >> 3);  // slot row
+        w_c[t] = (uint32_t)(((lane & 7) ^ f8d_swz(w_rho[t])) * 16);
+        const int32_t n = G1 ? col0 + (w_rho[t] & 63) : min(col0 + w_rho[t], N - 1);
+        w_off[t] = (uint32_t)n * (uint32_t)KD + w_c[t];
     }
-    // block-scale rows of the workgroup's 128-row block: [E][ceil(N / 128)][nst] per matrix
+    // block-scale rows of the workgroup's 128-row blocks: [E][ceil(N / 128)][nst] per matrix; the
+    // rows of consecutive GEMM-2 blocks follow each other, so stage u of the stream has scale u
     const int64_t srow = ((int64_t)g * ((N + 127) >> 7) + (col0 >> 7)) * nst;
     const float* fs0 = (G1 ? a.fsg : a.fsd) + srow;
     const float* fs1 = (G1 ? a.fsu : a.fsd) + srow;
@@ -475,20 +486,31 @@ __device__ __forceinline__ void stream_f8_dma_body(const GroupedArgs& a, int32_t
         const int64_t src = G1 ? (int64_t)row_token(a, r0 + rr) : (int64_t)(r0 + rr);
         arow[j] = abase + (src * lda + c * 8) * 2;
     }
-    auto issue = [&](int s) {
-        char* st = smem + (s % F8D_NS) * F8D_STAGE;
+    // stage u of the stream: block u / nst, reduction stage u % nst (GEMM-2 issues in order and
+    // counts them in ib, iks; GEMM-1 has one block)
+    int ib = 0, iks = 0;
+    auto issue = [&](int u) {
+        if constexpr (G1) iks = u;
+        char* st = smem + (u % F8D_NS) * F8D_STAGE;
         if (copier) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                __builtin_amdgcn_global_load_lds((const void*)(arow[j] + s * 256),
+                __builtin_amdgcn_global_load_lds((const void*)(arow[j] + iks * 256),
                                                  DSMOE_S_LDS(st + (wave * 4 + j) * 1024), 16, 0, 0);
         }
 #pragma unroll
         for (int t = 0; t < WT; ++t) {
             const int rho0 = (wave * WT + t) * 8;
             const char* wb = (G1 && rho0 >= 64) ? wb1 : wb0;
-            __builtin_amdgcn_global_load_lds((const void*)(wb + w_off[t] + s * 128),
+            uint32_t off = w_off[t];
+            if constexpr (!G1) {
+                if (ib > 0) off = (uint32_t)min(col0 + ib * CW + w_rho[t], N - 1) * (uint32_t)KD + w_c[t];
+            }
+            __builtin_amdgcn_global_load_lds((const void*)(wb + off + iks * 128),
                                              DSMOE_S_LDS(st + F8D_A_BYTES + rho0 * 128), 16, 0, 2 /* non-temporal */);
+        }
+        if constexpr (!G1) {
+            if (++iks == nst) iks = 0, ++ib;
         }
     };
 
@@ -496,9 +518,9 @@ __device__ __forceinline__ void stream_f8_dma_body(const GroupedArgs& a, int32_t
 #pragma unroll
     for (int m = 0; m < NW; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int q = lane >> 4, ln = lane & 15;
-    auto compute = [&](int s) {
-        const char* st = smem + (s % F8D_NS) * F8D_STAGE;
-        const float sc0 = *(const float*)(scl + s * 4), sc1 = *(const float*)(scl + 256 + s * 4);
+    auto compute = [&](int u) {
+        const char* st = smem + (u % F8D_NS) * F8D_STAGE;
+        const float sc0 = *(const float*)(scl + u * 4), sc1 = *(const float*)(scl + 256 + u * 4);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {  // four 32-k steps per stage
             const int p = t * 4 + q;   // the lane's 8-k piece of the stage
@@ -520,48 +542,69 @@ __device__ __forceinline__ void stream_f8_dma_body(const GroupedArgs& a, int32_t
         }
     };
 
+    // block b's results: GEMM-1 bf16(silu(gate) * up), GEMM-2 its two halves of 64 columns
+    auto epilogue = [&](int b) {
+        // the accumulators are read right after the last MFMAs, possibly behind the row-block
+        // branch: issue the MFMA-to-VALU wait states explicitly before any of them is read
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
+#pragma unroll
+        for (int m = 0; m < NW; ++m)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                if (m | rb) asm volatile("" : "+a"(acc[m][rb]));
+        const int32_t col = col0 + b * CW + wave * 16 + ln;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            if (rb >= nrb) break;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int32_t rr = rb * 16 + q * 4 + v;
+                if (rr >= cnt) continue;
+                if (G1) {
+                    ((bf16_t*)a.h)[(int64_t)(r0 + rr) * a.ldh + col] =
+                        f32_to_bf16(silu_f(acc[0][rb][v]) * acc[1][rb][v]);
+                } else {
+                    bf16_t* orow = (bf16_t*)a.o + (int64_t)(r0 + rr) * a.H;
+                    orow[col] = f32_to_bf16(acc[0][rb][v]);
+                    if (col + 64 < N) orow[col + 64] = f32_to_bf16(acc[1][rb][v]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NW; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
     // wave 0 (always a copier) copies the scale rows first; the first stage's wait covers them
     if (wave == 0) {
-        const int i = min(lane, nst - 1);
+        const int i = min(lane, ntot - 1);
         __builtin_amdgcn_global_load_lds((const void*)(fs0 + i), DSMOE_S_LDS(scl), 4, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(fs1 + i), DSMOE_S_LDS(scl + 256), 4, 0, 0);
     }
     issue(0);
-    if (nst > 1) issue(1);
-    for (int s = 0; s < nst; ++s) {
-        // stage s has landed for every wave; stage s+1 (if issued) may still be in flight
-        if (s + 1 < nst) {
+    if (ntot > 1) issue(1);
+    auto stage = [&](int u) {
+        // stage u has landed for every wave; stage u+1 (if issued) may still be in flight
+        if (u + 1 < ntot) {
             if (copier) f8d_wait_barrier<WT + 4>();  // wave-uniform; both arms hold one barrier
             else f8d_wait_barrier<WT>();
         } else {
             f8d_wait_barrier<0>();
         }
-        // the slot of stage s+2 held stage s-1, which every wave finished before this barrier
-        if (s + 2 < nst) issue(s + 2);
-        compute(s);
-    }
-    // the accumulators are read right after the last MFMAs, possibly behind the row-block
-    // branch: issue the MFMA-to-VALU wait states explicitly before any of them is read
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0][0]));
-#pragma unroll
-    for (int m = 0; m < NW; ++m)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-            if (m | rb) asm volatile("" : "+a"(acc[m][rb]));
-    const int32_t col = col0 + wave * 16 + ln;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        if (rb >= nrb) break;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int32_t rr = rb * 16 + q * 4 + v;
-            if (rr >= cnt) continue;
-            if (G1) {
-                ((bf16_t*)a.h)[(int64_t)(r0 + rr) * a.ldh + col] = f32_to_bf16(silu_f(acc[0][rb][v]) * acc[1][rb][v]);
-            } else {
-                bf16_t* orow = (bf16_t*)a.o + (int64_t)(r0 + rr) * a.H;
-                orow[col] = f32_to_bf16(acc[0][rb][v]);
-                if (col + 64 < N) orow[col + 64] = f32_to_bf16(acc[1][rb][v]);
+        // the slot of stage u+2 held stage u-1, which every wave finished before this barrier
+        if (u + 2 < ntot) issue(u + 2);
+        compute(u);
+    };
+    if constexpr (G1) {
+        for (int u = 0; u < ntot; ++u) stage(u);
+        epilogue(0);
+    } else {
+        int cks = 0, cbk = 0;  // block and reduction stage of the stage computed
+        for (int u = 0; u < ntot; ++u) {
+            stage(u);
+            if (++cks == nst) {
+                epilogue(cbk);
+                cks = 0;
+                ++cbk;
             }
         }
     }
@@ -575,18 +618,21 @@ __device__ __forceinline__ void stream_f8_dma_body(const GroupedArgs& a, int32_t
 // order, and the last group -- the shared expert, whose workgroups move twice the bytes of a
 // routed fp8 one, through registers -- would otherwise run alone at the end of the launch.
 template <bool G1>
-__global__ __launch_bounds__(256) void stream_f8(GroupedArgs a, int32_t g0) {
+__global__ __launch_bounds__(256) void stream_f8(GroupedArgs a, int32_t g0, int32_t nbw) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int32_t g = g0 + (int32_t)((blockIdx.y + gridDim.y - 1) % gridDim.y);
     int32_t r0, cnt;
     group_rows(a, g, r0, cnt);
     if (cnt <= 0 || cnt > a.stream_max_rows) return;  // workgroup-uniform
     if (g < a.E && cnt <= F8D_AROWS) {
-        stream_f8_dma_body<G1>(a, g, r0, cnt, smem);
+        stream_f8_dma_body<G1>(a, g, r0, cnt, G1 ? 1 : nbw, smem);
         return;
     }
-    const int32_t cb = G1 ? (int32_t)blockIdx.x : 2 * (int32_t)blockIdx.x;
-    for (int h = 0; h < (G1 ? 1 : 2); ++h) {
+    // the workgroup's columns in calls of 64: GEMM-1 workgroups own one block of 64 (nbw = 1),
+    // GEMM-2 ones nbw blocks of 128
+    const int32_t per = G1 ? 1 : 2 * nbw;
+    const int32_t cb = (int32_t)blockIdx.x * per;
+    for (int h = 0; h < per; ++h) {
         if (g == a.E) stream_body<WF_BF16, G1>(a, g, cb + h, smem);
         else stream_body<WF_F8, G1>(a, g, cb + h, smem);
     }
@@ -634,9 +680,14 @@ hipError_t launch_stream_f8(const GroupedArgs& a, bool gemm1, int32_t g0, int32_
     if (g1 <= g0) return hipSuccess;
     if (gemm1) {
         const int32_t N = max(a.I, a.Is);
-        hipLaunchKernelGGL((stream_f8<true>), dim3((N + 63) / 64, g1 - g0), dim3(256), F8D_LDS, s, a, g0);
+        hipLaunchKernelGGL((stream_f8<true>), dim3((N + 63) / 64, g1 - g0), dim3(256), F8D_LDS, s, a, g0, 1);
     } else {
-        hipLaunchKernelGGL((stream_f8<false>), dim3((a.H + 127) / 128, g1 - g0), dim3(256), F8D_LDS, s, a, g0);
+        // GEMM-2 reductions are short (I / 128 stages): two column blocks per workgroup when
+        // their stages fit the scale buffer
+        const int32_t nbw = (a.I / 128) * 2 <= F8D_MAX_STAGES ? 2 : 1;
+        const int32_t nblk = (a.H + 127) / 128;
+        hipLaunchKernelGGL((stream_f8<false>), dim3((nblk + nbw - 1) / nbw, g1 - g0), dim3(256), F8D_LDS, s, a, g0,
+                           nbw);
     }
     return hipGetLastError();
 }
