@@ -78,6 +78,10 @@ __global__ __launch_bounds__(SD_THREADS) void stream_dma(GroupedArgs a, int32_t 
     if (col0 >= N) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int nst = KD >> 6;
+    // GEMM-2 weight rows are I * 2 bytes apart, a power of two for the usual I: when every
+    // workgroup in flight fetches the same line offset of its rows, the loads crowd a few memory
+    // channels.  Each GEMM-2 workgroup therefore starts its pass over k at its own stage and wraps.
+    const int rot = G1 ? 0 : (int)((blockIdx.x * 7u) % (unsigned)nst);
 
     // weight rows: uniform bases (64-bit) plus per-lane 32-bit byte offsets
     const char* wbase[2];
@@ -118,7 +122,9 @@ __global__ __launch_bounds__(SD_THREADS) void stream_dma(GroupedArgs a, int32_t 
         const bool copier = wave < nrb;  // wave-uniform
         auto issue = [&](int s) {
             char* st = smem + (s % SD_NS) * ST;
-            const int32_t kb = s * 128;  // byte offset of the stage's 64 k
+            int sr = s + rot;
+            if (sr >= nst) sr -= nst;
+            const int32_t kb = sr * 128;  // byte offset of the stage's 64 k
             if (copier) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
