@@ -158,6 +158,9 @@ EDGE = [
     # step; I = 192: output blocks of 128 and 64), tiled, tiled with long groups, softmax + gate
     ("fp8_small", C1.with_(T=50, expert="fp8", planted=0)),
     ("fp8_tail", C1.with_(T=20, H=320, I=192, Is=192, expert="fp8", planted=0)),
+    # fp8 decode through the DMA ring with an odd number of 128-column down blocks (H = 384: the
+    # last down workgroup owns one block) and two-stage reductions
+    ("fp8_stream_odd_blocks", C1.with_(T=40, H=384, I=256, Is=128, expert="fp8", planted=0)),
     ("tiled_fp8", C1.with_(T=400, H=512, I=256, Is=192, expert="fp8", planted=0)),
     ("tiled_fp8_ragged_blocks", C1.with_(T=500, H=320, I=192, Is=128, expert="fp8", planted=0)),
     ("tiled_rows_fp8", C1.with_(T=2048, H=256, I=128, Is=128, expert="fp8", planted=0)),
