@@ -87,8 +87,8 @@ struct TileArgs {
 // list, or only the routed or only the shared part of it, so that a launch over one part spreads
 // that part over every XCD) times col_tiles items, in bands of CB column tiles (measured: 2 for
 // the bf16 gate/up kernel and 8 for the bf16 down projection, whose 256 x 256 tiles hold 144 KB
-// of LDS, one per CU; 16 for the 4-bit and 8 for the fp8 kernel, two per CU, whose small groups
-// put few row tiles in a band): items of one
+// of LDS, one per CU; 16 for the 4-bit gate/up kernel, 32 for its down projection and 8 for the
+// fp8 kernel, two per CU, whose small groups put few row tiles in a band): items of one
 // band walk the row tiles with the column fastest, so the workgroups running at once share both A
 // panels (same rows) and B panels (same group and columns).  Workgroup ids congruent mod 8 land
 // on the same XCD; each XCD takes one contiguous eighth of the logical space, sized by the tile
@@ -794,7 +794,7 @@ __global__ __launch_bounds__(THREADS) void gemm_dma_wq(TileArgs ta) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const GroupedArgs& a = ta.a;
     int32_t tile, ct;
-    if (!map_tile<WQ == WQ_Q4 ? 16 : 8>(ta, tile, ct)) return;
+    if (!map_tile<WQ == WQ_Q4 ? (SWIGLU ? 16 : 32) : 8>(ta, tile, ct)) return;
     const i32x4 ti = *(const i32x4*)(ta.tile_info + 4 * tile);  // group, first row, group rows
     const int32_t g = ti[0], m0 = ti[1], r0 = ti[2], cnt = ti[3];
     if (g < ta.g0 || g >= ta.g1 || g >= a.E) return;  // routed groups only (the shared expert is bf16)
