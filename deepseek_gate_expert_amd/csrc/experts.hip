@@ -1,4 +1,4 @@
-// experts.hip - grouped SwiGLU expert GEMMs on bf16 MFMA (bf16 or 4-bit weights).
+// experts.hip - grouped SwiGLU expert GEMMs on bf16 MFMA (bf16, 4-bit or fp8 weights).
 //
 // Role: the per-expert matmuls that gather_mm / gather_qmm perform in the reference design
 // (page "Epic: Engine Inference Core Stage E - MoE + hybrid families", opening paragraph), with
@@ -8,8 +8,10 @@
 // for every row r of group g (rows come from the dispatch; group E is the shared expert, whose
 // rows TK + t are the tokens in order).
 //
-// This file holds the weight-streaming kernel ("stream"), for groups of up to 64 rows -- the
-// decode regime, where the layer is bound by HBM bandwidth.  A workgroup of four wavefronts
+// This file holds the weight-streaming kernels for groups of up to 64 rows -- the decode regime,
+// where the layer is bound by HBM bandwidth: the register-streaming kernel ("stream") described
+// here, and for fp8 layers a kernel that moves the codes of small groups through an LDS DMA ring
+// (stream_f8, further down) and runs the register-streaming body for the rest.  A workgroup of four wavefronts
 // owns 64 output columns of one group; each wavefront owns 16 of them and reads its weight
 // rows from HBM exactly once per 64-row chunk of the group, straight into registers, two
 // 128-element steps ahead of the MFMAs that consume them (three for fp8 and for the bf16 down
